@@ -1,0 +1,15 @@
+"""Oracle package: plain fp64 CPU reference of the parallel block.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library.
+"""
+from .block import (  # noqa: F401
+    block_forward,
+    block_forward_rows,
+    gelu,
+    layer_norm,
+    relative_error,
+    split_projection,
+    swa_attention,
+    window_lo,
+)

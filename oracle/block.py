@@ -1,0 +1,181 @@
+"""Oracle: a plain fp64 CPU forward of the parallel transformer block with
+sliding-window causal attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The library's product path never
+calls it, and it shares no code with the HIP path: the only thing both sides
+use is the seeded input generator in ``workload``.
+
+What it computes, and where the pages define it (MegaScale guided reading on
+the ai-training-network-primer site):
+  * section 2 "Changing the model to help the system": the parallel block feeds
+    the attention and feed-forward sub-layers from the same input and sums their
+    outputs; sliding-window attention lets each token attend only to a fixed
+    window of nearby tokens;
+  * section 3 "Overlap in all three dimensions" (tensor and sequence
+    parallelism): a layer-norm precedes the parallel linear layers, and with
+    tensor parallelism each GPU holds a slice of heads and FFN columns whose
+    partial outputs are summed by a reduce-scatter;
+  * section 4 "Operators, data pipeline, and starting up": attention is exact
+    (FlashAttention-2), LayerNorm and GeLU are the named operators.
+
+Readings where the pages are silent (each listed with its reason in the design
+notes): one LayerNorm output feeds both branches; biased variance, eps = 1e-5,
+affine gamma/beta; exact erf GeLU; window = keys j in [i-W+1, i], W keys
+including the query itself, never crossing a sequence; scale 1/sqrt(hd); no
+positional encoding, no biases, no dropout; the residual x is added unless the
+caller asks for the tensor-parallel partial.
+
+Every array is promoted to float64 on entry; nothing is rounded in between.
+Matrix products use numpy's ``@`` (a library routine) and the error function
+comes from scipy.  Attention is evaluated per slab of queries against only the
+keys that can fall in their windows, with an explicit band mask, so its cost
+grows with S*W rather than S^2.
+
+Pins (all in the CPU test-suite): dense brute-force band attention, W >= S vs
+torch's causal attention, W = 1 closed form, 2-key closed form, the branch-sum
+identity, LayerNorm and GeLU against torch and math.erf, tensor-parallel
+decomposition, locality, and hand-derived closed-form blocks.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf
+
+
+def layer_norm(x, gamma, beta, eps: float):
+    """LayerNorm over the last axis: (x - mean) / sqrt(biased var + eps) * gamma + beta."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+
+
+def gelu(z):
+    """Exact GeLU: z * Phi(z) = z/2 * (1 + erf(z / sqrt(2)))."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def window_lo(i: int, W: int) -> int:
+    """First key position query i may attend to (inclusive); the last is i."""
+    return max(0, i - W + 1)
+
+
+def swa_attention(q, k, v, W: int, q_pos0: int = 0, k_pos0: int = 0, slab: int = 128):
+    """Sliding-window causal softmax attention for one sequence.
+
+    q: [Sq, H, hd] holding positions q_pos0 .. q_pos0+Sq-1.
+    k, v: [Sk, H, hd] holding positions k_pos0 .. k_pos0+Sk-1; they must cover
+    every key the queries' windows reach.
+    Query at position i attends to keys j with i-W+1 <= j <= i; scores are
+    q_i . k_j / sqrt(hd) and the weights are their softmax over the window.
+    Returns [Sq, H, hd].
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    Sq, H, hd = q.shape
+    out = np.zeros_like(q)
+    scale = 1.0 / math.sqrt(hd)
+    for s0 in range(0, Sq, slab):
+        s1 = min(Sq, s0 + slab)
+        i0, i1 = q_pos0 + s0, q_pos0 + s1 - 1  # absolute query positions in the slab
+        j0 = window_lo(i0, W)
+        j1 = i1
+        if j0 < k_pos0 or j1 >= k_pos0 + k.shape[0]:
+            raise ValueError("keys do not cover the queries' windows")
+        kk = k[j0 - k_pos0:j1 - k_pos0 + 1]  # [L, H, hd]
+        vv = v[j0 - k_pos0:j1 - k_pos0 + 1]
+        qi = np.arange(i0, i1 + 1)[:, None]
+        kj = np.arange(j0, j1 + 1)[None, :]
+        allowed = (kj <= qi) & (kj >= qi - W + 1)  # [slab, L]
+        qs = q[s0:s1].transpose(1, 0, 2)  # [H, slab, hd]
+        scores = (qs @ kk.transpose(1, 2, 0)) * scale  # [H, slab, L]
+        scores = np.where(allowed[None], scores, -np.inf)
+        m = scores.max(axis=-1, keepdims=True)
+        p = np.exp(scores - m)
+        p /= p.sum(axis=-1, keepdims=True)
+        out[s0:s1] = (p @ vv.transpose(1, 0, 2)).transpose(1, 0, 2)
+    return out
+
+
+def split_projection(z, H: int, hd: int):
+    """Split u @ W_in^T into Q, K, V (each [..., H, hd]) and the FC1 pre-activation."""
+    A = H * hd
+    lead = z.shape[:-1]
+    q = z[..., 0:A].reshape(*lead, H, hd)
+    k = z[..., A:2 * A].reshape(*lead, H, hd)
+    v = z[..., 2 * A:3 * A].reshape(*lead, H, hd)
+    f = z[..., 3 * A:]
+    return q, k, v, f
+
+
+def block_forward(x, gamma, beta, w_in, w_out, H: int, hd: int, W: int,
+                  eps: float = 1e-5, add_residual: bool = True, return_parts: bool = False):
+    """y = [x +] ( Attn_SWA(LN x) || GeLU(LN x W_fc1^T) ) W_out^T for x [B, S, d].
+
+    The attention heads and the GeLU activations sit side by side and go
+    through one output projection, which is the sum of the attention
+    out-projection and FC2 (W_out's columns are [heads ; FC2]).
+    """
+    x = np.asarray(x, np.float64)
+    w_in = np.asarray(w_in, np.float64)
+    w_out = np.asarray(w_out, np.float64)
+    B, S, d = x.shape
+    A = H * hd
+    u = layer_norm(x, gamma, beta, eps)
+    z = u @ w_in.T
+    q, k, v, f = split_projection(z, H, hd)
+    o = np.empty((B, S, H, hd))
+    for b in range(B):
+        o[b] = swa_attention(q[b], k[b], v[b], W)
+    g = gelu(f)
+    ag = np.concatenate([o.reshape(B, S, A), g], axis=-1)
+    y = ag @ w_out.T
+    if add_residual:
+        y = y + x
+    if return_parts:
+        return y, dict(u=u, qkv=z[..., :3 * A], ag=ag)
+    return y
+
+
+def block_forward_rows(x, gamma, beta, w_in, w_out, H: int, hd: int, W: int, row_blocks,
+                       eps: float = 1e-5, add_residual: bool = True):
+    """Output rows y[b, i0:i1] for each (b, i0, i1) in ``row_blocks``.
+
+    Only the LayerNorm rows, projections and keys those queries need are
+    formed (keys i0-W+1 .. i1-1), so full-size workloads can be checked on
+    samples.  Returns a list of [i1-i0, d] arrays.
+    """
+    w_in = np.asarray(w_in, np.float64)
+    w_out = np.asarray(w_out, np.float64)
+    A = H * hd
+    outs = []
+    for b, i0, i1 in row_blocks:
+        j0 = window_lo(i0, W)
+        xs = np.asarray(x[b, j0:i1], np.float64)
+        u = layer_norm(xs, gamma, beta, eps)
+        z_kv = u @ w_in[A:3 * A].T
+        k = z_kv[:, :A].reshape(-1, H, hd)
+        v = z_kv[:, A:].reshape(-1, H, hd)
+        uq = u[i0 - j0:]
+        q = (uq @ w_in[:A].T).reshape(-1, H, hd)
+        f = uq @ w_in[3 * A:].T
+        o = swa_attention(q, k, v, W, q_pos0=i0, k_pos0=j0)
+        ag = np.concatenate([o.reshape(-1, A), gelu(f)], axis=-1)
+        y = ag @ w_out.T
+        if add_residual:
+            y = y + xs[i0 - j0:]
+        outs.append(y)
+    return outs
+
+
+def relative_error(y_test, y_ref) -> float:
+    """max |y_test - y_ref| / max |y_ref| (the parity metric)."""
+    y_test = np.asarray(y_test, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    denom = np.abs(y_ref).max()
+    return float(np.abs(y_test - y_ref).max() / denom) if denom > 0 else float(np.abs(y_test).max())

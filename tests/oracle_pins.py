@@ -1,0 +1,333 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each ``pin_*`` function takes an oracle module (``oracle.block`` or a copy of
+it with a planted mistake) and raises AssertionError when the oracle disagrees
+with brute force, a closed form, an invariant or a library routine.  The
+reference values come from, in turn:
+  * pure-Python loops over single query/key pairs (brute force);
+  * torch CPU float64 library routines (layer_norm, gelu, scaled-dot-product
+    attention with an explicit band mask or is_causal);
+  * closed forms: W = 1 (each token sees only itself), W = 2 (a two-key softmax
+    is a logistic function), uniform attention when Q is zero, LayerNorm of
+    zero-mean unit-variance sign patterns, the normal CDF at 1;
+  * invariants: branch-sum identity, tensor-parallel decomposition, locality of
+    the window, batch independence.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+PHI_1 = 0.8413447460685429  # standard normal CDF at 1 (textbook table value)
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _rand_block(seed, B, S, d, H, hd, ffn, affine=True):
+    rng = _rng(seed)
+    x = rng.standard_normal((B, S, d)) * 1.3 + 0.4
+    w_in = rng.standard_normal((3 * H * hd + ffn, d)) * (1.0 / math.sqrt(d))
+    w_out = rng.standard_normal((d, H * hd + ffn)) * (1.0 / math.sqrt(H * hd + ffn))
+    if affine:
+        gamma = 1.0 + 0.3 * rng.standard_normal(d)
+        beta = 0.2 * rng.standard_normal(d)
+    else:
+        gamma, beta = np.ones(d), np.zeros(d)
+    return x, gamma, beta, w_in, w_out
+
+
+def _torch_band_attention(q, k, v, W):
+    """q, k, v: [S, H, hd] numpy fp64 -> torch SDPA with a boolean band mask."""
+    S = q.shape[0]
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    mask = (j <= i) & (j > i - W)
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2)))[None] for a in (q, k, v))
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+def _torch_block(x, gamma, beta, w_in, w_out, H, hd, W, eps, add_residual=True):
+    """The block assembled from torch float64 library routines."""
+    tx = torch.from_numpy(x)
+    A = H * hd
+    u = F.layer_norm(tx, (x.shape[-1],), torch.from_numpy(gamma), torch.from_numpy(beta), eps)
+    z = u @ torch.from_numpy(w_in).T
+    B, S, _ = x.shape
+    q = z[..., :A].reshape(B, S, H, hd).transpose(1, 2)
+    k = z[..., A:2 * A].reshape(B, S, H, hd).transpose(1, 2)
+    v = z[..., 2 * A:3 * A].reshape(B, S, H, hd).transpose(1, 2)
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    mask = (j <= i) & (j > i - W)
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask).transpose(1, 2).reshape(B, S, A)
+    wo = torch.from_numpy(w_out)
+    y = o @ wo[:, :A].T + F.gelu(z[..., 3 * A:], approximate="none") @ wo[:, A:].T
+    if add_residual:
+        y = y + tx
+    return y.numpy()
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def pin_attention_brute_force(ob):
+    """Blocked band attention == per-pair Python loops, for odd S and several W."""
+    rng = _rng(11)
+    for S, H, hd in ((1, 1, 4), (37, 2, 8), (133, 1, 4)):
+        q = rng.standard_normal((S, H, hd))
+        k = rng.standard_normal((S, H, hd))
+        v = rng.standard_normal((S, H, hd))
+        for W in sorted({1, 2, 7, max(1, S - 1), S, 2 * S}):
+            got = ob.swa_attention(q, k, v, W, slab=16)
+            for h in range(H):
+                for i in range(S):
+                    keys = [j for j in range(S) if j <= i and i - j < W]
+                    s = [sum(q[i, h, t] * k[j, h, t] for t in range(hd)) / math.sqrt(hd) for j in keys]
+                    mx = max(s)
+                    e = [math.exp(a - mx) for a in s]
+                    den = sum(e)
+                    for t in range(hd):
+                        ref = sum(e[n] * v[keys[n], h, t] for n in range(len(keys))) / den
+                        assert abs(got[i, h, t] - ref) <= 1e-12 * (1 + abs(ref)), (S, W, h, i, t)
+
+
+def pin_attention_vs_torch_band(ob):
+    """Band attention == torch SDPA with an explicit boolean band mask."""
+    rng = _rng(12)
+    for S, W in ((300, 1), (300, 37), (300, 128), (257, 256), (129, 500)):
+        q, k, v = (rng.standard_normal((S, 3, 16)) for _ in range(3))
+        got = ob.swa_attention(q, k, v, W)
+        ref = _torch_band_attention(q, k, v, W)
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_attention_full_causal(ob):
+    """W >= S is plain causal attention (torch SDPA is_causal=True)."""
+    rng = _rng(13)
+    S = 211
+    q, k, v = (rng.standard_normal((S, 2, 16)) for _ in range(3))
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2)))[None] for a in (q, k, v))
+    ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True)[0].numpy().transpose(1, 0, 2)
+    for W in (S, S + 1, 4 * S):
+        np.testing.assert_allclose(ob.swa_attention(q, k, v, W), ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_attention_w1_is_identity(ob):
+    """W = 1: each query sees only its own key, so the output is its own value."""
+    rng = _rng(14)
+    q, k, v = (rng.standard_normal((77, 3, 8)) * 5 for _ in range(3))
+    np.testing.assert_allclose(ob.swa_attention(q, k, v, 1), v, rtol=0, atol=1e-13)
+
+
+def pin_attention_two_keys(ob):
+    """W = 2: o_i = s(delta) v_i + (1 - s(delta)) v_{i-1}, s = logistic,
+    delta = (q_i.k_i - q_i.k_{i-1}) / sqrt(hd); o_0 = v_0."""
+    rng = _rng(15)
+    S, H, hd = 50, 2, 8
+    q, k, v = (rng.standard_normal((S, H, hd)) for _ in range(3))
+    got = ob.swa_attention(q, k, v, 2, slab=7)
+    for h in range(H):
+        np.testing.assert_allclose(got[0, h], v[0, h], atol=1e-14)
+        for i in range(1, S):
+            delta = (q[i, h] @ k[i, h] - q[i, h] @ k[i - 1, h]) / math.sqrt(hd)
+            w = 1.0 / (1.0 + math.exp(-delta))
+            np.testing.assert_allclose(got[i, h], w * v[i, h] + (1 - w) * v[i - 1, h], rtol=1e-12, atol=1e-13)
+
+
+def pin_attention_offset_keys(ob):
+    """Queries given at an offset with only their needed keys == the full call."""
+    rng = _rng(16)
+    S, W = 200, 33
+    q, k, v = (rng.standard_normal((S, 2, 8)) for _ in range(3))
+    full = ob.swa_attention(q, k, v, W)
+    i0, i1 = 120, 170
+    j0 = i0 - W + 1
+    part = ob.swa_attention(q[i0:i1], k[j0:i1], v[j0:i1], W, q_pos0=i0, k_pos0=j0)
+    np.testing.assert_allclose(part, full[i0:i1], rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- LN, GeLU
+
+
+def pin_layer_norm(ob):
+    """LayerNorm == torch layer_norm; gamma=1, beta=0 rows have mean 0 and
+    variance var/(var+eps)."""
+    rng = _rng(21)
+    x = rng.standard_normal((5, 7, 96)) * 3 + 2
+    g = 1 + 0.5 * rng.standard_normal(96)
+    b = 0.3 * rng.standard_normal(96)
+    for eps in (1e-5, 0.1):
+        ref = F.layer_norm(torch.from_numpy(x), (96,), torch.from_numpy(g), torch.from_numpy(b), eps).numpy()
+        np.testing.assert_allclose(ob.layer_norm(x, g, b, eps), ref, rtol=1e-12, atol=1e-12)
+    eps = 0.5
+    u = ob.layer_norm(x, np.ones(96), np.zeros(96), eps)
+    var = x.var(axis=-1)
+    np.testing.assert_allclose(u.mean(axis=-1), 0, atol=1e-12)
+    np.testing.assert_allclose(u.var(axis=-1), var / (var + eps), rtol=1e-12)
+
+
+def pin_gelu(ob):
+    """GeLU == torch exact gelu and x*Phi(x) via math.erf; odd-part identity;
+    GeLU(0) = 0; GeLU(1) = Phi(1)."""
+    z = np.linspace(-9, 9, 2001)
+    ref = F.gelu(torch.from_numpy(z), approximate="none").numpy()
+    got = ob.gelu(z)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+    loop = np.array([t * 0.5 * (1 + math.erf(t / math.sqrt(2))) for t in z])
+    np.testing.assert_allclose(got, loop, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(ob.gelu(-z), got - z, rtol=1e-12, atol=1e-12)
+    assert ob.gelu(np.array([0.0]))[0] == 0.0
+    assert abs(ob.gelu(np.array([1.0]))[0] - PHI_1) < 1e-15
+    # the tanh approximation differs visibly at z ~ 2.7: the exact form is the one computed
+    tanh_form = 0.5 * 2.7 * (1 + math.tanh(math.sqrt(2 / math.pi) * (2.7 + 0.044715 * 2.7 ** 3)))
+    assert abs(ob.gelu(np.array([2.7]))[0] - tanh_form) > 1e-4
+
+
+# ----------------------------------------------------------------------------- whole block
+
+
+def pin_block_vs_torch(ob):
+    """Whole block == the same block assembled from torch fp64 library routines,
+    with odd shapes, several windows, random gamma/beta."""
+    for seed, (B, S, d, H, hd, ffn), W in ((31, (2, 45, 24, 3, 8, 40), 9),
+                                           (32, (1, 70, 32, 2, 16, 48), 70),
+                                           (33, (3, 17, 16, 1, 8, 8), 1)):
+        x, g, b, wi, wo = _rand_block(seed, B, S, d, H, hd, ffn)
+        for add_res in (True, False):
+            got = ob.block_forward(x, g, b, wi, wo, H, hd, W, eps=1e-5, add_residual=add_res)
+            ref = _torch_block(x, g, b, wi, wo, H, hd, W, 1e-5, add_res)
+            np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+
+
+def pin_block_w1_closed_form(ob):
+    """W = 1: the attention branch is the linear map (u W_v^T) W_o^T."""
+    B, S, d, H, hd, ffn = 2, 19, 24, 3, 4, 20
+    x, g, b, wi, wo = _rand_block(41, B, S, d, H, hd, ffn)
+    A = H * hd
+    u = F.layer_norm(torch.from_numpy(x), (d,), torch.from_numpy(g), torch.from_numpy(b), 1e-5).numpy()
+    ref = x + (u @ wi[2 * A:3 * A].T) @ wo[:, :A].T \
+        + F.gelu(torch.from_numpy(u @ wi[3 * A:].T)).numpy() @ wo[:, A:].T
+    got = ob.block_forward(x, g, b, wi, wo, H, hd, 1)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_block_branch_sum(ob):
+    """Parallel block == sum of its separately computed branches: the attention
+    branch alone (FC1 rows zero, so GeLU(0) = 0) plus the MLP branch alone
+    (V rows zero, so attention outputs 0)."""
+    B, S, d, H, hd, ffn, W = 2, 40, 32, 2, 8, 48, 11
+    x, g, b, wi, wo = _rand_block(51, B, S, d, H, hd, ffn)
+    A = H * hd
+    full = ob.block_forward(x, g, b, wi, wo, H, hd, W)
+    wi_attn = wi.copy()
+    wi_attn[3 * A:] = 0
+    wi_mlp = wi.copy()
+    wi_mlp[2 * A:3 * A] = 0
+    y_attn = ob.block_forward(x, g, b, wi_attn, wo, H, hd, W, add_residual=False)
+    y_mlp = ob.block_forward(x, g, b, wi_mlp, wo, H, hd, W, add_residual=False)
+    np.testing.assert_allclose(full - x, y_attn + y_mlp, rtol=1e-11, atol=1e-12)
+    assert np.abs(y_attn).max() > 1e-3 and np.abs(y_mlp).max() > 1e-3
+
+
+def pin_block_tensor_parallel(ob):
+    """Split heads and FFN columns over R shards; the shards' partials plus x
+    reproduce the unsharded block (the reduce-scatter's sum)."""
+    B, S, d, H, hd, ffn, W = 1, 33, 16, 4, 4, 32, 6
+    x, g, b, wi, wo = _rand_block(61, B, S, d, H, hd, ffn)
+    A = H * hd
+    full = ob.block_forward(x, g, b, wi, wo, H, hd, W)
+    for R in (2, 4):
+        hs, fs = H // R, ffn // R
+        total = np.zeros_like(full)
+        for r in range(R):
+            rows = []
+            for part in range(3):  # Q, K, V slices of this shard's heads
+                rows.append(wi[part * A + r * hs * hd: part * A + (r + 1) * hs * hd])
+            rows.append(wi[3 * A + r * fs: 3 * A + (r + 1) * fs])
+            wi_r = np.concatenate(rows, axis=0)
+            wo_r = np.concatenate([wo[:, r * hs * hd:(r + 1) * hs * hd], wo[:, A + r * fs:A + (r + 1) * fs]], axis=1)
+            total += ob.block_forward(x, g, b, wi_r, wo_r, hs, hd, W, add_residual=False)
+        np.testing.assert_allclose(total + x, full, rtol=1e-11, atol=1e-12)
+
+
+def pin_block_locality(ob):
+    """Perturbing tokens outside query i's window leaves y_i bit-identical;
+    perturbing inside changes it; batches are independent."""
+    B, S, d, H, hd, ffn, W = 2, 40, 16, 2, 8, 16, 5
+    x, g, b, wi, wo = _rand_block(71, B, S, d, H, hd, ffn)
+    y = ob.block_forward(x, g, b, wi, wo, H, hd, W)
+    bump = 3.0 * _rng(72).standard_normal(d)  # not a constant: LayerNorm removes constant shifts
+    i = 25
+    for j in (i - W, i + 1, 0, S - 1):
+        xp = x.copy()
+        xp[0, j] += bump
+        yp = ob.block_forward(xp, g, b, wi, wo, H, hd, W)
+        assert np.array_equal(yp[0, i], y[0, i]), j
+        assert np.array_equal(yp[1], y[1])
+    for j in (i - W + 1, i - 1):
+        xp = x.copy()
+        xp[0, j] += bump
+        yp = ob.block_forward(xp, g, b, wi, wo, H, hd, W)
+        assert np.abs(yp[0, i] - y[0, i]).max() > 1e-6, j
+
+
+def pin_block_uniform_closed_form(ob):
+    """Hand-derived block.  Rows of x are m + s*p with p a zero-mean, unit-
+    variance sign pattern, so with eps = 0 LayerNorm returns gamma*p + beta.
+    With W_q = 0 every score is 0 and attention is the plain mean of V over the
+    window; W_v = I and W_fc1 = I, W_out = [I | I] give
+        y_i = x_i + mean_{j in window(i)} u_j + GeLU(u_i),
+    and GeLU(+1) = Phi(1), GeLU(-1) = Phi(1) - 1."""
+    d = hd = ffn = 4
+    H = 1
+    pats = np.array([[1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1], [-1, 1, 1, -1], [-1, -1, 1, 1]], float)
+    S = len(pats)
+    m = np.array([0.5, -2.0, 3.0, 0.0, 1.25])
+    s = np.array([2.0, 0.5, 1.0, 3.0, 0.25])
+    x = (m[:, None] + s[:, None] * pats)[None]
+    eye = np.eye(4)
+    w_in = np.concatenate([np.zeros((4, 4)), 0.7 * eye[::-1], eye, eye], axis=0)  # Q=0, K arbitrary, V=I, FC1=I
+    w_out = np.concatenate([eye, eye], axis=1)
+    g1 = {1.0: PHI_1, -1.0: PHI_1 - 1.0}
+    for W in (1, 2, 3, 5):
+        y = ob.block_forward(x, np.ones(d), np.zeros(d), w_in, w_out, H, hd, W, eps=0.0)
+        for i in range(S):
+            lo = max(0, i - W + 1)
+            mean_u = pats[lo:i + 1].mean(axis=0)
+            ref = x[0, i] + mean_u + np.array([g1[v] for v in pats[i]])
+            np.testing.assert_allclose(y[0, i], ref, rtol=0, atol=1e-13)
+
+
+def pin_rows_match_full(ob):
+    """Row-sampled forward == full forward on the same rows."""
+    B, S, d, H, hd, ffn, W = 2, 90, 16, 2, 8, 24, 13
+    x, g, b, wi, wo = _rand_block(81, B, S, d, H, hd, ffn)
+    full = ob.block_forward(x, g, b, wi, wo, H, hd, W)
+    blocks = [(0, 0, 7), (1, 5, 30), (1, 60, 90), (0, 12, 13)]
+    for (bb, i0, i1), y in zip(blocks, ob.block_forward_rows(x, g, b, wi, wo, H, hd, W, blocks)):
+        np.testing.assert_allclose(y, full[bb, i0:i1], rtol=1e-12, atol=1e-13)
+
+
+ALL_PINS = [
+    pin_attention_brute_force,
+    pin_attention_vs_torch_band,
+    pin_attention_full_causal,
+    pin_attention_w1_is_identity,
+    pin_attention_two_keys,
+    pin_attention_offset_keys,
+    pin_layer_norm,
+    pin_gelu,
+    pin_block_vs_torch,
+    pin_block_w1_closed_form,
+    pin_block_branch_sum,
+    pin_block_tensor_parallel,
+    pin_block_locality,
+    pin_block_uniform_closed_form,
+    pin_rows_match_full,
+]

@@ -1,0 +1,70 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and require that
+at least one pin catches each of them.  This is what makes the pins a real
+check: a dropped term, a wrong sign or index, an off-by-one window or a
+swapped operand must not slip through."""
+import os
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "block.py")
+
+MUTANTS = {
+    "unbiased_variance": [("var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)",
+                           "var = ((x - mu) ** 2).sum(axis=-1, keepdims=True) / (x.shape[-1] - 1)")],
+    "eps_outside_sqrt": [("np.sqrt(var + eps)", "(np.sqrt(var) + eps)")],
+    "dropped_beta": [(" + np.asarray(beta, np.float64)", "")],
+    "dropped_gamma": [(" * np.asarray(gamma, np.float64)", "")],
+    "gelu_tanh_form": [("0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))",
+                        "0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))")],
+    "gelu_missing_sqrt2": [("erf(z / math.sqrt(2.0))", "erf(z)")],
+    "window_one_too_wide": [("max(0, i - W + 1)", "max(0, i - W)"),
+                            ("(kj >= qi - W + 1)", "(kj >= qi - W)")],
+    "window_one_too_narrow": [("(kj >= qi - W + 1)", "(kj >= qi - W + 2)")],
+    "window_not_causal": [("(kj <= qi)", "(kj <= qi + 1)")],
+    "scale_1_over_hd": [("1.0 / math.sqrt(hd)", "1.0 / hd")],
+    "no_scale": [("scale = 1.0 / math.sqrt(hd)", "scale = 1.0")],
+    "k_v_swapped": [("k = z[..., A:2 * A]", "k = z[..., 2 * A:3 * A]"),
+                    ("v = z[..., 2 * A:3 * A]", "v = z[..., A:2 * A]")],
+    "head_minor_layout": [("q = z[..., 0:A].reshape(*lead, H, hd)",
+                           "q = z[..., 0:A].reshape(*lead, hd, H).swapaxes(-1, -2)")],
+    "concat_order_swapped": [("np.concatenate([o.reshape(B, S, A), g], axis=-1)",
+                              "np.concatenate([g, o.reshape(B, S, A)], axis=-1)")],
+    "gelu_on_attention_too": [("ag = np.concatenate([o.reshape(B, S, A), g], axis=-1)",
+                               "ag = gelu(np.concatenate([o.reshape(B, S, A), f], axis=-1))")],
+    "residual_dropped": [("        y = y + x\n", "        y = y\n")],
+    "residual_of_ln_output": [("        y = y + x\n", "        y = y + u\n")],
+    "w_out_not_transposed": [("y = ag @ w_out.T", "y = ag @ w_out.reshape(w_out.shape[1], w_out.shape[0])")],
+    "softmax_over_all_keys": [("scores = np.where(allowed[None], scores, -np.inf)", "scores = scores")],
+}
+
+
+def _mutant(edits):
+    src = open(SRC_PATH).read()
+    for old, new in edits:
+        assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    mod = _mutant(MUTANTS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+            break
+    assert caught, f"no pin caught the planted mistake {name}"
+
+
+def test_unmutated_copy_passes():
+    mod = _mutant([])
+    for pin in ALL_PINS:
+        pin(mod)
