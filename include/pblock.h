@@ -1,0 +1,163 @@
+/*
+ * pblock.h -- C ABI of the MI355X (gfx950) forward pass of one parallel
+ * transformer block with sliding-window causal attention:
+ *
+ *     y = [x +] Attn_SWA(LN(x)) + MLP(LN(x))
+ *
+ * Source of the method: the MegaScale guided reading on the
+ * ai-training-network-primer site.  Section 2 ("Changing the model to help the
+ * system") defines the parallel block (attention and feed-forward fed from the
+ * same input, outputs summed) and sliding-window attention (each token attends
+ * to a fixed window of nearby tokens).  Section 3 (tensor and sequence
+ * parallelism) places a layer-norm before the parallel linear layers and a
+ * reduce-scatter of partial sums after them.  Section 4 ("Operators") names
+ * the operators: exact attention, LayerNorm, GeLU.
+ *
+ * Readings of what the pages leave open (fixed here for every entry point):
+ *   - one LayerNorm output u = LN(x) feeds both branches; biased variance,
+ *     eps from the cfg (1e-5 by default), affine gamma/beta;
+ *   - GeLU is the exact erf form z/2 * (1 + erf(z / sqrt 2));
+ *   - query i attends to keys j with max(0, i-W+1) <= j <= i (W keys, itself
+ *     included); windows never cross sequences; W >= S is full causal;
+ *   - scores are q.k / sqrt(hd); no positional encoding, no biases, no dropout.
+ *
+ * Layouts (all row-major, contiguous, caller-owned DEVICE memory):
+ *   x, out   [B, S, d]                       (token-major)
+ *   ln_gamma, ln_beta  [d]
+ *   w_in     [3*H*hd + ffn, d]   rows = [Q heads; K heads; V heads; FC1],
+ *                                 each head's hd rows contiguous, head-major
+ *   w_out    [d, H*hd + ffn]     columns = [attention heads (head-major); FC2]
+ * Element type: PBLOCK_BF16 (all of x, gamma, beta, w_in, w_out, out are
+ * bf16) or PBLOCK_F32 (all fp32: the debug path).  Accumulation is fp32 in
+ * both; bf16 intermediates are rounded to nearest even.
+ *
+ * Errors: every function returns PBLOCK_OK (0) or a negative pblock_status.
+ * All argument checks run before anything is enqueued; on error nothing is
+ * launched and `out` is untouched.  Faults inside kernels are asynchronous and
+ * surface at the caller's next synchronisation of the stream.  No C++
+ * exception crosses this boundary.  pblock_last_error() gives the detail of
+ * the most recent failure on the calling thread.
+ */
+#ifndef PBLOCK_H
+#define PBLOCK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PBLOCK_OK = 0,
+  PBLOCK_ERR_NULL = -1,          /* a required pointer is NULL */
+  PBLOCK_ERR_SHAPE = -2,         /* a dimension is out of the supported range */
+  PBLOCK_ERR_DTYPE = -3,         /* dtype is neither PBLOCK_F32 nor PBLOCK_BF16 */
+  PBLOCK_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned */
+  PBLOCK_ERR_ALIAS = -5,         /* out overlaps x or a weight */
+  PBLOCK_ERR_CFG_MISMATCH = -6,  /* forward cfg incompatible with the handle's */
+  PBLOCK_ERR_DEVICE = -7,        /* no gfx950 device current */
+  PBLOCK_ERR_NOMEM = -8,         /* workspace allocation failed */
+  PBLOCK_ERR_HIP = -9,           /* a HIP runtime call or launch failed */
+  PBLOCK_ERR_ARG = -10           /* any other invalid argument */
+} pblock_status;
+
+typedef enum { PBLOCK_F32 = 0, PBLOCK_BF16 = 1 } pblock_dtype;
+
+/* Block shape.  Supported ranges (else PBLOCK_ERR_SHAPE):
+ *   B >= 1, S >= 1, B*S <= 2^24;  W >= 1 (W >= S means full causal);
+ *   hd in {64, 128};  H >= 1;  d, H*hd, ffn positive multiples of 64;
+ *   d <= 32768.
+ * add_residual: 1 -> y = x + branches; 0 -> y = branches only (the partial
+ * sum one tensor-parallel shard contributes to the reduce-scatter).
+ * ln_eps > 0. */
+typedef struct {
+  int32_t B, S, d, H, hd, ffn, W;
+  int32_t dtype;
+  int32_t add_residual;
+  float ln_eps;
+} pblock_cfg;
+
+typedef struct {
+  const void* ln_gamma; /* [d] */
+  const void* ln_beta;  /* [d] */
+  const void* w_in;     /* [3*H*hd + ffn, d] */
+  const void* w_out;    /* [d, H*hd + ffn] */
+} pblock_weights;
+
+typedef struct pblock_s* pblock_t;
+
+/* Validates cfg (host only, touches no device).  Returns 0 or an error. */
+int pblock_validate_cfg(const pblock_cfg* cfg);
+
+/* Bytes of device workspace a handle for cfg allocates (u, QKV, AG buffers),
+ * or a negative status.  Host only. */
+int64_t pblock_workspace_bytes(const pblock_cfg* cfg);
+
+/* Algorithmic FLOPs of one forward for cfg: 2*M*d*(3*H*hd+ffn) +
+ * 2*M*(H*hd+ffn)*d + 4*B*H*hd*sum_i min(i+1, W), M = B*S.  Host only;
+ * returns a negative value for an invalid cfg. */
+double pblock_flops(const pblock_cfg* cfg);
+
+/* Creates a handle on the current HIP device: validates cfg, checks the device
+ * is gfx950, and allocates the workspace (hipMalloc) sized for cfg's B*S.  The
+ * handle owns the workspace until pblock_destroy.  *out_handle is set only on
+ * success. */
+int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle);
+
+/* Enqueues the block forward on `stream` (a hipStream_t; NULL = the null
+ * stream) and returns without synchronising.  x, the weights and out are
+ * device pointers owned by the caller; they must stay valid until the stream
+ * passes this work.  cfg must equal the create cfg except that B and S may
+ * differ as long as B*S does not exceed the create cfg's B*S.  A handle's
+ * workspace is shared by its calls: do not run one handle on two streams at
+ * once.  out must not overlap x or any weight. */
+int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg,
+                   void* out, void* stream);
+
+/* Frees the workspace and the handle.  NULL is a no-op.  The caller must have
+ * synchronised every stream the handle was used on. */
+int pblock_destroy(pblock_t h);
+
+/* Static description of a status code. */
+const char* pblock_strerror(int code);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char* pblock_last_error(void);
+
+/* Device pointers of the handle's intermediates after a forward, for
+ * stage-by-stage inspection (owned by the handle, valid until destroy):
+ *   u   [B*S, d]            LayerNorm output
+ *   qkv [B*S, 3*H*hd]       Q | K | V projections (head-major within each)
+ *   ag  [B*S, H*hd + ffn]   attention output (head-major) | GeLU(FC1)
+ * Any of the out-pointers may be NULL. */
+int pblock_intermediates(pblock_t h, void** u, void** qkv, void** ag);
+
+/* Copies the intermediates of the handle's most recent forward (its B*S rows)
+ * into caller-owned device buffers laid out as above, enqueued on `stream`.
+ * Any destination may be NULL (skipped).  Returns PBLOCK_ERR_ARG if no forward
+ * has run on the handle. */
+int pblock_copy_intermediates(pblock_t h, void* u, void* qkv, void* ag, void* stream);
+
+/* Per-kernel timing.  When enabled, pblock_forward records HIP events around
+ * each of its launches on the forward's stream; pblock_kernel_times then
+ * synchronises on the last recorded event and returns the summed milliseconds
+ * per kernel since the last reset, in the order [layernorm, gemm_in,
+ * attention, gemm_out], plus the number of forwards timed.  Enabling or
+ * disabling resets the sums.  n must be >= 4. */
+int pblock_set_timing(pblock_t h, int enable);
+int pblock_kernel_times(pblock_t h, float* ms, int n, int* n_forwards);
+
+/* Sliding-window attention on its own (the same kernel pblock_forward runs).
+ *   qkv  [B*S, ld_qkv]: Q at columns [0, H*hd), K at [H*hd, 2*H*hd),
+ *        V at [2*H*hd, 3*H*hd); ld_qkv >= 3*H*hd, a multiple of 8.
+ *   o    [B*S, ld_o]: head h written to columns [h*hd, (h+1)*hd); ld_o >= H*hd,
+ *        a multiple of 8.
+ * dtype as above; hd in {64, 128}.  Enqueued on `stream`, no sync. */
+int pblock_swa_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, int32_t B, int32_t S,
+                         int32_t H, int32_t hd, int32_t W, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PBLOCK_H */

@@ -1,0 +1,68 @@
+"""Helpers shared by the GPU tests: moving seeded inputs to the device and
+running the block through the C ABI."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}  # max|y_gpu - y_ref| / max|y_ref|
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr: np.ndarray, dtype: str):
+    import torch
+
+    if dtype == "bf16":
+        a = np.ascontiguousarray(arr)
+        assert a.dtype == np.uint16
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def from_dev(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def upload(inp):
+    cfg = inp.cfg
+    arrs = inp.device_arrays()
+    return {k: to_dev(v, cfg.dtype) for k, v in arrs.items()}
+
+
+def run_block(cfg, dev, handle=None, want_parts=False):
+    """Forward on the GPU; returns y (float64 numpy [B, S, d]) and optionally u, qkv, ag."""
+    import torch
+
+    import transformer_block_fwd_amd as tb
+
+    own = handle is None
+    h = tb.pblock_create(cfg) if own else handle
+    try:
+        out = torch.empty_like(dev["x"])
+        tb.pblock_forward(h, dev["x"], (dev["gamma"], dev["beta"], dev["w_in"], dev["w_out"]), cfg, out)
+        parts = None
+        if want_parts:
+            tdt = dev["x"].dtype
+            M = cfg.B * cfg.S
+            u = torch.empty((M, cfg.d), dtype=tdt, device="cuda")
+            qkv = torch.empty((M, 3 * cfg.A), dtype=tdt, device="cuda")
+            ag = torch.empty((M, cfg.k_out), dtype=tdt, device="cuda")
+            tb.pblock_copy_intermediates(h, u, qkv, ag)
+            parts = dict(u=from_dev(u), qkv=from_dev(qkv), ag=from_dev(ag))
+        torch.cuda.synchronize()
+        y = from_dev(out).reshape(cfg.B, cfg.S, cfg.d)
+    finally:
+        if own:
+            tb.pblock_destroy(h)
+    return (y, parts) if want_parts else y
+
+
+def rel_err(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.abs(a - b).max() / np.abs(b).max())

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max|y_gpu - y_ref| / max|y_ref| <= 1e-2 for bf16 and <= 1e-4 for fp32,
+elementwise over every output (small shapes) or over sampled row blocks that
+the oracle computes one by one (full-size workloads, in the same launch
+configuration the benchmark times).  Invariants that hold at any size are
+checked bit-for-bit where the arithmetic makes them exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import TOL, from_dev, log, rel_err, run_block, to_dev, upload
+from workload import CONFIGS, BlockConfig, make_inputs, sample_row_blocks
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+import transformer_block_fwd_amd as tb  # noqa: E402
+
+
+def oracle_y(inp):
+    c = inp.cfg
+    return oracle.block_forward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, c.H, c.hd, c.W,
+                                eps=c.ln_eps, add_residual=bool(c.add_residual))
+
+
+SMALL = [
+    # name, B, S, d, H, hd, ffn, W, dtype, affine, add_residual
+    ("bf16_ragged", 2, 200, 256, 2, 128, 320, 37, "bf16", True, 1),
+    ("bf16_hd64", 1, 333, 192, 3, 64, 128, 100, "bf16", True, 1),
+    ("bf16_w1", 1, 130, 128, 2, 64, 64, 1, "bf16", False, 1),
+    ("bf16_w2", 2, 97, 128, 1, 128, 64, 2, "bf16", True, 1),
+    ("bf16_w_ge_s_partial", 3, 129, 256, 2, 128, 256, 1000, "bf16", True, 0),
+    ("bf16_one_token", 1, 1, 64, 1, 64, 64, 4, "bf16", True, 1),
+    ("bf16_window_edges", 1, 515, 256, 2, 128, 128, 64, "bf16", True, 1),
+    ("bf16_window_65", 1, 300, 256, 2, 128, 128, 65, "bf16", True, 1),
+    ("bf16_multi_tile", 1, 700, 512, 4, 128, 768, 300, "bf16", True, 1),
+    ("bf16_big_ragged_m", 4, 1000, 2048, 16, 128, 8192, 256, "bf16", False, 1),
+    ("bf16_big_ntail", 3, 1100, 1024, 8, 128, 2112, 200, "bf16", True, 1),
+    ("f32_ragged", 2, 77, 128, 2, 64, 192, 9, "f32", True, 1),
+    ("f32_hd128", 1, 150, 256, 2, 128, 128, 64, "f32", True, 0),
+    ("f32_w1", 1, 40, 64, 1, 64, 64, 1, "f32", True, 1),
+]
+
+
+def small_cfg(name, B, S, d, H, hd, ffn, W, dtype, affine, add_res):
+    return BlockConfig(name, B=B, S=S, d=d, H=H, hd=hd, ffn=ffn, W=W, dtype=dtype, add_residual=add_res), affine
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes_full(case):
+    cfg, affine = small_cfg(*case)
+    log(f"[case] {cfg}")
+    inp = make_inputs(cfg, seed=3, affine=affine)
+    y = run_block(cfg, upload(inp))
+    err = rel_err(y, oracle_y(inp))
+    log(f"[parity] {cfg.name}: rel err {err:.3e} (tol {TOL[cfg.dtype]})")
+    assert err <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[1], SMALL[11], SMALL[12]], ids=lambda c: c[0])
+def test_stage_parity(case):
+    """LayerNorm output, Q|K|V, and [attention | GeLU] each against the oracle's."""
+    cfg, affine = small_cfg(*case)
+    log(f"[case] stages {cfg}")
+    inp = make_inputs(cfg, seed=4, affine=affine)
+    y, parts = run_block(cfg, upload(inp), want_parts=True)
+    y_ref, ref = oracle.block_forward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W,
+                                      eps=cfg.ln_eps, add_residual=bool(cfg.add_residual), return_parts=True)
+    tol = TOL[cfg.dtype]
+    M = cfg.M
+    for name in ("u", "qkv", "ag"):
+        err = rel_err(parts[name], ref[name].reshape(M, -1))
+        log(f"[parity] {cfg.name} stage {name}: {err:.3e}")
+        assert err <= tol, name
+    assert rel_err(y, y_ref) <= tol
+
+
+def test_tiny_config_fp32():
+    cfg = CONFIGS["tiny"]
+    log(f"[case] {cfg}")
+    inp = make_inputs(cfg, seed=0)
+    y = run_block(cfg, upload(inp))
+    err = rel_err(y, oracle_y(inp))
+    log(f"[parity] tiny: {err:.3e}")
+    assert err <= TOL["f32"]
+
+
+def test_small_config_full():
+    cfg = CONFIGS["small"]
+    log(f"[case] {cfg}")
+    inp = make_inputs(cfg, seed=0)
+    y = run_block(cfg, upload(inp))
+    err = rel_err(y, oracle_y(inp))
+    log(f"[parity] small: {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["shard175b", "long", "fullcausal"])
+def test_large_config_sampled(name):
+    """Full-size workloads: sampled row blocks (sequence start, first full
+    window, a random block, sequence end; first and last batch)."""
+    cfg = CONFIGS[name]
+    log(f"[case] {cfg}")
+    inp = make_inputs(cfg, seed=0)
+    dev = upload(inp)
+    y = run_block(cfg, dev)
+    del dev
+    torch.cuda.empty_cache()
+    assert np.isfinite(y).all()
+    blocks = sample_row_blocks(cfg)
+    refs = oracle.block_forward_rows(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W, blocks,
+                                     eps=cfg.ln_eps, add_residual=bool(cfg.add_residual))
+    got = np.concatenate([y[b, i0:i1] for b, i0, i1 in blocks])
+    ref = np.concatenate(refs)
+    err = rel_err(got, ref)
+    log(f"[parity] {name}: {len(blocks)} row blocks, rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_branch_sum_on_gpu():
+    """y - x == attention branch alone (FC1 rows zero) + MLP branch alone (V rows zero)."""
+    cfg = BlockConfig("branches", B=2, S=160, d=256, H=2, hd=128, ffn=384, W=40, dtype="bf16")
+    inp = make_inputs(cfg, seed=5, affine=True)
+    dev = upload(inp)
+    A = cfg.A
+    y_full = run_block(cfg, dev)
+    part = cfg.replace(add_residual=0)
+    w_attn = dev["w_in"].clone()
+    w_attn[3 * A:] = 0
+    w_mlp = dev["w_in"].clone()
+    w_mlp[2 * A:3 * A] = 0
+    y_attn = run_block(part, {**dev, "w_in": w_attn})
+    y_mlp = run_block(part, {**dev, "w_in": w_mlp})
+    err = rel_err(y_attn + y_mlp, y_full - inp.x)
+    log(f"[parity] branch sum: {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.abs(y_attn).max() > 1e-3 and np.abs(y_mlp).max() > 1e-3
+
+
+@pytest.mark.parametrize("R", [2, 4])
+def test_tensor_parallel_partials_on_gpu(R):
+    """R shards (heads and FFN columns split) emitting partials: sum + x == unsharded y."""
+    cfg = BlockConfig("tp", B=1, S=256, d=512, H=4, hd=128, ffn=1024, W=64, dtype="bf16")
+    inp = make_inputs(cfg, seed=6)
+    A = cfg.A
+    y_full = oracle_y(inp)
+    hs, fs = cfg.H // R, cfg.ffn // R
+    total = np.zeros_like(y_full)
+    for r in range(R):
+        rows = [inp.bits["w_in"][p * A + r * hs * cfg.hd: p * A + (r + 1) * hs * cfg.hd] for p in range(3)]
+        rows.append(inp.bits["w_in"][3 * A + r * fs: 3 * A + (r + 1) * fs])
+        wi = np.concatenate(rows, axis=0)
+        wo = np.concatenate([inp.bits["w_out"][:, r * hs * cfg.hd:(r + 1) * hs * cfg.hd],
+                             inp.bits["w_out"][:, A + r * fs:A + (r + 1) * fs]], axis=1)
+        sc = cfg.replace(H=hs, ffn=fs, add_residual=0)
+        dev = {"x": to_dev(inp.bits["x"], "bf16"), "gamma": to_dev(inp.bits["gamma"], "bf16"),
+               "beta": to_dev(inp.bits["beta"], "bf16"), "w_in": to_dev(wi, "bf16"), "w_out": to_dev(wo, "bf16")}
+        total += run_block(sc, dev)
+    err = rel_err(total + inp.x, y_full)
+    log(f"[parity] tp R={R}: {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_window_locality_bitwise():
+    """Changing tokens outside query i's window leaves y_i bit-identical; other
+    batches are untouched."""
+    cfg = BlockConfig("loc", B=2, S=300, d=256, H=2, hd=128, ffn=256, W=50, dtype="bf16")
+    inp = make_inputs(cfg, seed=7)
+    dev = upload(inp)
+    y0 = run_block(cfg, dev)
+    i = 200
+    x2 = dev["x"].clone()
+    x2[0, i - cfg.W] = torch.randn(cfg.d, device="cuda").to(torch.bfloat16)
+    x2[0, i + 1] = torch.randn(cfg.d, device="cuda").to(torch.bfloat16)
+    y1 = run_block(cfg, {**dev, "x": x2})
+    assert np.array_equal(y1[0, i], y0[0, i])
+    assert np.array_equal(y1[1], y0[1])
+    assert np.abs(y1[0, i + 1] - y0[0, i + 1]).max() > 0
+    x3 = dev["x"].clone()
+    x3[0, i - cfg.W + 1] = torch.randn(cfg.d, device="cuda").to(torch.bfloat16)
+    y2 = run_block(cfg, {**dev, "x": x3})
+    assert np.abs(y2[0, i] - y0[0, i]).max() > 0
+
+
+def test_w1_attention_is_value_copy():
+    """W = 1: the attention output equals the value projection bit for bit."""
+    cfg = BlockConfig("w1", B=2, S=100, d=128, H=2, hd=128, ffn=128, W=1, dtype="bf16")
+    inp = make_inputs(cfg, seed=8, affine=True)
+    _, parts = run_block(cfg, upload(inp), want_parts=True)
+    A = cfg.A
+    assert np.array_equal(parts["ag"][:, :A], parts["qkv"][:, 2 * A:3 * A])
+
+
+def test_window_covering_sequence_is_causal_bitwise():
+    """W = S and W = 3S run the same band path and give identical outputs."""
+    cfg = BlockConfig("ws", B=2, S=320, d=256, H=2, hd=128, ffn=256, W=320, dtype="bf16")
+    inp = make_inputs(cfg, seed=9)
+    dev = upload(inp)
+    ya = run_block(cfg, dev)
+    yb = run_block(cfg.replace(W=3 * cfg.S), dev)
+    assert np.array_equal(ya, yb)
+    assert rel_err(ya, oracle_y(inp)) <= TOL["bf16"]
+
+
+ATTN_CASES = [(1, 1), (2, 1), (64, 64), (65, 64), (127, 63), (128, 129), (300, 1), (300, 2), (300, 63), (300, 64),
+              (300, 65), (513, 128), (513, 300), (700, 700), (1000, 1)]
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_attention_entry_point(hd):
+    """pblock_swa_attention against the oracle's band attention over many (S, W)."""
+    rng = np.random.Generator(np.random.PCG64(10))
+    H, B = 2, 2
+    A = H * hd
+    for S, W in ATTN_CASES:
+        qkv = (rng.standard_normal((B * S, 3 * A), dtype=np.float32) * 1.5).astype(np.float32)
+        qkv_t = torch.from_numpy(qkv).cuda().to(torch.bfloat16)
+        o = torch.zeros((B * S, A), dtype=torch.bfloat16, device="cuda")
+        tb.pblock_swa_attention(qkv_t, 3 * A, o, A, B, S, H, hd, W, "bf16")
+        torch.cuda.synchronize()
+        qv = from_dev(qkv_t).reshape(B, S, 3, H, hd)
+        ref = np.stack([oracle.swa_attention(qv[b, :, 0], qv[b, :, 1], qv[b, :, 2], W) for b in range(B)])
+        err = rel_err(from_dev(o).reshape(B, S, H, hd), ref)
+        log(f"[parity] attention hd={hd} S={S} W={W}: {err:.3e}")
+        assert err <= TOL["bf16"], (S, W)
+
+
+def test_attention_entry_fp32():
+    rng = np.random.Generator(np.random.PCG64(11))
+    B, S, H, hd, W = 1, 200, 2, 64, 33
+    A = H * hd
+    qkv = rng.standard_normal((B * S, 3 * A)).astype(np.float32)
+    qkv_t = torch.from_numpy(qkv).cuda()
+    o = torch.zeros((B * S, A), dtype=torch.float32, device="cuda")
+    tb.pblock_swa_attention(qkv_t, 3 * A, o, A, B, S, H, hd, W, "f32")
+    torch.cuda.synchronize()
+    qv = qkv.astype(np.float64).reshape(B, S, 3, H, hd)
+    ref = oracle.swa_attention(qv[0, :, 0], qv[0, :, 1], qv[0, :, 2], W)
+    assert rel_err(from_dev(o).reshape(S, H, hd), ref) <= TOL["f32"]
+
+
+def test_deterministic_and_reusable_handle():
+    """Same inputs -> bit-identical outputs; a handle serves a smaller B*S."""
+    cfg = BlockConfig("det", B=4, S=128, d=256, H=2, hd=128, ffn=256, W=32, dtype="bf16")
+    inp = make_inputs(cfg, seed=12)
+    dev = upload(inp)
+    h = tb.pblock_create(cfg)
+    try:
+        y1 = run_block(cfg, dev, handle=h)
+        y2 = run_block(cfg, dev, handle=h)
+        assert np.array_equal(y1, y2)
+        small = cfg.replace(B=2)
+        dev2 = {**dev, "x": dev["x"][:2].contiguous()}
+        y3 = run_block(small, dev2, handle=h)
+        assert np.array_equal(y3, y1[:2])
+        with pytest.raises(tb.PblockError) as ei:
+            run_block(cfg.replace(B=5), {**dev, "x": torch.cat([dev["x"], dev["x"][:1]])}, handle=h)
+        assert ei.value.code == tb._abi.PBLOCK_ERR_CFG_MISMATCH
+    finally:
+        tb.pblock_destroy(h)
+
+
+def test_errors_leave_output_untouched():
+    cfg = BlockConfig("err", B=1, S=64, d=128, H=1, hd=64, ffn=64, W=8, dtype="bf16")
+    inp = make_inputs(cfg, seed=13)
+    dev = upload(inp)
+    h = tb.pblock_create(cfg)
+    try:
+        out = torch.full_like(dev["x"], 7.0)
+        w = (dev["gamma"], dev["beta"], dev["w_in"], dev["w_out"])
+        with pytest.raises(tb.PblockError) as ei:
+            tb.pblock_forward(h, dev["x"], w, cfg.replace(d=192), out)
+        assert ei.value.code == tb._abi.PBLOCK_ERR_CFG_MISMATCH
+        with pytest.raises(tb.PblockError) as ei:
+            tb.pblock_forward(h, dev["x"], w, cfg, dev["x"])
+        assert ei.value.code == tb._abi.PBLOCK_ERR_ALIAS
+        torch.cuda.synchronize()
+        assert bool((out == 7.0).all())
+    finally:
+        tb.pblock_destroy(h)
+
+
+def test_kernel_timing_api():
+    cfg = BlockConfig("timing", B=1, S=512, d=512, H=4, hd=128, ffn=1024, W=128, dtype="bf16")
+    inp = make_inputs(cfg, seed=14)
+    dev = upload(inp)
+    h = tb.pblock_create(cfg)
+    try:
+        tb.pblock_set_timing(h, True)
+        for _ in range(3):
+            run_block(cfg, dev, handle=h)
+        ms, n = tb.pblock_kernel_times(h)
+        assert n == 3
+        assert all(v > 0 for v in ms.values()), ms
+    finally:
+        tb.pblock_destroy(h)

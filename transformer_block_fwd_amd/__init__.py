@@ -1,0 +1,191 @@
+"""Python binding of the pblock C ABI (include/pblock.h).
+
+Forward pass of one parallel transformer block with sliding-window causal
+attention on an MI355X (gfx950):
+
+    y = [x +] Attn_SWA(LN(x)) + MLP(LN(x))
+
+Every step runs in the HIP library; this module only marshals arguments
+(torch tensors -> device pointers, the current torch stream -> hipStream_t)
+and turns error codes into exceptions.  Function names mirror the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _abi
+from ._abi import PBLOCK_BF16, PBLOCK_F32, PblockCfg, PblockError, PblockWeights  # noqa: F401
+
+__all__ = [
+    "PBLOCK_BF16", "PBLOCK_F32", "PblockCfg", "PblockError", "PblockWeights", "ParallelBlock", "make_cfg",
+    "pblock_validate_cfg", "pblock_workspace_bytes", "pblock_flops", "pblock_create", "pblock_forward",
+    "pblock_destroy", "pblock_intermediates", "pblock_copy_intermediates", "pblock_set_timing",
+    "pblock_kernel_times", "pblock_swa_attention", "pblock_strerror", "pblock_last_error", "KERNEL_NAMES",
+]
+
+KERNEL_NAMES = ("layernorm", "gemm_in", "attention", "gemm_out")
+
+_DTYPES = {"bf16": PBLOCK_BF16, "f32": PBLOCK_F32, PBLOCK_BF16: PBLOCK_BF16, PBLOCK_F32: PBLOCK_F32}
+
+
+def make_cfg(B, S, d, H, hd, ffn, W, dtype="bf16", add_residual=1, ln_eps=1e-5) -> PblockCfg:
+    return PblockCfg(int(B), int(S), int(d), int(H), int(hd), int(ffn), int(W), _DTYPES[dtype],
+                     int(add_residual), float(ln_eps))
+
+
+def as_cfg(cfg) -> PblockCfg:
+    """A PblockCfg, or any object with B, S, d, H, hd, ffn, W, dtype (and
+    optionally add_residual, ln_eps) attributes."""
+    if isinstance(cfg, PblockCfg):
+        return cfg
+    return make_cfg(cfg.B, cfg.S, cfg.d, cfg.H, cfg.hd, cfg.ffn, cfg.W, cfg.dtype,
+                    getattr(cfg, "add_residual", 1), getattr(cfg, "ln_eps", 1e-5))
+
+
+def _ptr(t) -> int:
+    """Device pointer of a torch tensor (must be contiguous and on a GPU) or an int."""
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _check_tensor(t, name, dtype_code, numel):
+    if t is None or isinstance(t, int):
+        return
+    import torch
+
+    want = torch.bfloat16 if dtype_code == PBLOCK_BF16 else torch.float32
+    if t.dtype != want:
+        raise TypeError(f"{name} must be {want}, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def pblock_strerror(code: int) -> str:
+    return _abi.lib().pblock_strerror(int(code)).decode()
+
+
+def pblock_last_error() -> str:
+    return _abi.last_error()
+
+
+def pblock_validate_cfg(cfg) -> int:
+    c = as_cfg(cfg)
+    return _abi.lib().pblock_validate_cfg(ctypes.byref(c))
+
+
+def pblock_workspace_bytes(cfg) -> int:
+    c = as_cfg(cfg)
+    v = _abi.lib().pblock_workspace_bytes(ctypes.byref(c))
+    _abi.check(v if v < 0 else 0, "pblock_workspace_bytes")
+    return v
+
+
+def pblock_flops(cfg) -> float:
+    c = as_cfg(cfg)
+    return _abi.lib().pblock_flops(ctypes.byref(c))
+
+
+def pblock_create(cfg) -> int:
+    c = as_cfg(cfg)
+    h = ctypes.c_void_p()
+    _abi.check(_abi.lib().pblock_create(ctypes.byref(c), ctypes.byref(h)), "pblock_create")
+    return h.value
+
+
+def pblock_destroy(handle: int) -> None:
+    _abi.check(_abi.lib().pblock_destroy(ctypes.c_void_p(handle)), "pblock_destroy")
+
+
+def pblock_forward(handle: int, x, weights, cfg, out, stream=None) -> None:
+    """weights = (ln_gamma, ln_beta, w_in, w_out); all tensors contiguous on the GPU."""
+    c = as_cfg(cfg)
+    gamma, beta, w_in, w_out = weights
+    M, A = c.B * c.S, c.H * c.hd
+    for t, name, n in ((x, "x", M * c.d), (out, "out", M * c.d), (gamma, "ln_gamma", c.d), (beta, "ln_beta", c.d),
+                       (w_in, "w_in", (3 * A + c.ffn) * c.d), (w_out, "w_out", c.d * (A + c.ffn))):
+        _check_tensor(t, name, c.dtype, n)
+    w = PblockWeights(_ptr(gamma), _ptr(beta), _ptr(w_in), _ptr(w_out))
+    _abi.check(_abi.lib().pblock_forward(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), ctypes.byref(c),
+                                         _ptr(out), _stream(stream)), "pblock_forward")
+
+
+def pblock_intermediates(handle: int) -> tuple[int, int, int]:
+    u, qkv, ag = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+    _abi.check(_abi.lib().pblock_intermediates(ctypes.c_void_p(handle), ctypes.byref(u), ctypes.byref(qkv),
+                                               ctypes.byref(ag)), "pblock_intermediates")
+    return u.value, qkv.value, ag.value
+
+
+def pblock_copy_intermediates(handle: int, u=None, qkv=None, ag=None, stream=None) -> None:
+    _abi.check(_abi.lib().pblock_copy_intermediates(ctypes.c_void_p(handle), _ptr(u), _ptr(qkv), _ptr(ag),
+                                                    _stream(stream)), "pblock_copy_intermediates")
+
+
+def pblock_set_timing(handle: int, enable: bool) -> None:
+    _abi.check(_abi.lib().pblock_set_timing(ctypes.c_void_p(handle), int(bool(enable))), "pblock_set_timing")
+
+
+def pblock_kernel_times(handle: int) -> tuple[dict, int]:
+    """Summed milliseconds per kernel since timing was enabled, and the forward count."""
+    ms = (ctypes.c_float * 4)()
+    n = ctypes.c_int()
+    _abi.check(_abi.lib().pblock_kernel_times(ctypes.c_void_p(handle), ms, 4, ctypes.byref(n)),
+               "pblock_kernel_times")
+    return dict(zip(KERNEL_NAMES, [float(v) for v in ms])), n.value
+
+
+def pblock_swa_attention(qkv, ld_qkv, o, ld_o, B, S, H, hd, W, dtype="bf16", stream=None) -> None:
+    _abi.check(_abi.lib().pblock_swa_attention(_ptr(qkv), int(ld_qkv), _ptr(o), int(ld_o), int(B), int(S), int(H),
+                                               int(hd), int(W), _DTYPES[dtype], _stream(stream)),
+               "pblock_swa_attention")
+
+
+class ParallelBlock:
+    """Owns a pblock handle (and so its workspace) for one block shape."""
+
+    def __init__(self, cfg):
+        self.cfg = as_cfg(cfg)
+        self.handle = pblock_create(self.cfg)
+
+    def forward(self, x, gamma, beta, w_in, w_out, out=None, cfg=None, stream=None):
+        import torch
+
+        c = as_cfg(cfg) if cfg is not None else self.cfg
+        if out is None:
+            out = torch.empty_like(x)
+        pblock_forward(self.handle, x, (gamma, beta, w_in, w_out), c, out, stream)
+        return out
+
+    def close(self):
+        if self.handle:
+            pblock_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass

@@ -1,0 +1,491 @@
+// C ABI of the parallel-block forward (declared in include/pblock.h).
+//
+// pblock_forward enqueues four kernels on the caller's stream:
+//   1. layernorm_kernel          x -> u
+//   2. GEMM (split/GeLU epi)     u . W_in^T -> Q|K|V into `qkv`, GeLU(FC1) into ag[:, A:]
+//   3. swa_attn kernel           qkv -> attention heads into ag[:, :A]
+//   4. GEMM (residual epi)       ag . W_out^T (+ x) -> out
+// The attention output and the GeLU activations share one K-contiguous buffer
+// (ag), so the out-projection and FC2 run as a single GEMM: the two branches
+// of the parallel block are summed inside its accumulators.
+#include <hip/hip_runtime.h>
+
+#include <array>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/pblock.h"
+#include "attn_bf16.hpp"
+#include "attn_f32.hpp"
+#include "gemm_bf16.hpp"
+#include "gemm_f32.hpp"
+#include "layernorm.hpp"
+
+using namespace pblk;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int elem_size(int32_t dtype) { return dtype == PBLOCK_BF16 ? 2 : 4; }
+
+bool mult64(int64_t v) { return v > 0 && (v % 64) == 0; }
+
+int validate(const pblock_cfg* c) {
+  if (!c) return fail(PBLOCK_ERR_NULL, "cfg is NULL");
+  if (c->dtype != PBLOCK_F32 && c->dtype != PBLOCK_BF16) return fail(PBLOCK_ERR_DTYPE, "dtype must be F32 or BF16");
+  if (c->B < 1 || c->S < 1) return fail(PBLOCK_ERR_SHAPE, "B and S must be >= 1");
+  if (int64_t(c->B) * c->S > (int64_t(1) << 24)) return fail(PBLOCK_ERR_SHAPE, "B*S exceeds 2^24");
+  if (c->W < 1) return fail(PBLOCK_ERR_SHAPE, "W must be >= 1");
+  if (c->hd != 64 && c->hd != 128) return fail(PBLOCK_ERR_SHAPE, "hd must be 64 or 128");
+  if (c->H < 1 || c->H > 4096) return fail(PBLOCK_ERR_SHAPE, "H must be in [1, 4096]");
+  if (!mult64(c->d) || c->d > 32768) return fail(PBLOCK_ERR_SHAPE, "d must be a positive multiple of 64, <= 32768");
+  if (!mult64(c->ffn) || c->ffn > (1 << 20)) return fail(PBLOCK_ERR_SHAPE, "ffn must be a positive multiple of 64, <= 2^20");
+  if (int64_t(c->H) * c->hd > (1 << 20)) return fail(PBLOCK_ERR_SHAPE, "H*hd exceeds 2^20");
+  if (c->add_residual != 0 && c->add_residual != 1) return fail(PBLOCK_ERR_ARG, "add_residual must be 0 or 1");
+  if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps)) return fail(PBLOCK_ERR_ARG, "ln_eps must be finite and > 0");
+  return PBLOCK_OK;
+}
+
+struct Dims {
+  int64_t M, A, n_in, k_out;
+};
+Dims dims(const pblock_cfg* c) {
+  Dims d;
+  d.M = int64_t(c->B) * c->S;
+  d.A = int64_t(c->H) * c->hd;
+  d.n_in = 3 * d.A + c->ffn;
+  d.k_out = d.A + c->ffn;
+  return d;
+}
+
+int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+struct WsLayout {
+  int64_t u, qkv, ag, total;
+};
+WsLayout ws_layout(const pblock_cfg* c) {
+  const Dims dm = dims(c);
+  const int es = elem_size(c->dtype);
+  WsLayout w;
+  w.u = 0;
+  w.qkv = align256(dm.M * c->d * es);
+  w.ag = w.qkv + align256(dm.M * 3 * dm.A * es);
+  w.total = w.ag + align256(dm.M * dm.k_out * es);
+  return w;
+}
+
+// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, -1 no.
+int g_arch_ok[64];
+
+int check_device(int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PBLOCK_ERR_DEVICE, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(PBLOCK_ERR_DEVICE, "device index out of range");
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(PBLOCK_ERR_DEVICE, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    g_arch_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  if (g_arch_ok[dev] != 1) return fail(PBLOCK_ERR_DEVICE, "current device is not gfx950");
+  if (dev_out) *dev_out = dev;
+  return PBLOCK_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + uintptr_t(nb) && b0 < a0 + uintptr_t(na);
+}
+
+int launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return PBLOCK_OK;
+}
+
+// ------------------------------------------------------------------------ launches
+
+template <typename T>
+void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d, float eps, hipStream_t s) {
+  const int per = 16 / int(sizeof(T));
+  const int need = (d / per + kLnThreads - 1) / kLnThreads;
+  const dim3 grid{static_cast<unsigned>(M)}, block{kLnThreads};
+  if (need <= 1) hipLaunchKernelGGL((layernorm_kernel<T, 1>), grid, block, 0, s, x, g, b, u, d, eps);
+  else if (need <= 2) hipLaunchKernelGGL((layernorm_kernel<T, 2>), grid, block, 0, s, x, g, b, u, d, eps);
+  else if (need <= 4) hipLaunchKernelGGL((layernorm_kernel<T, 4>), grid, block, 0, s, x, g, b, u, d, eps);
+  else if (need <= 8) hipLaunchKernelGGL((layernorm_kernel<T, 8>), grid, block, 0, s, x, g, b, u, d, eps);
+  else if (need <= 16) hipLaunchKernelGGL((layernorm_kernel<T, 16>), grid, block, 0, s, x, g, b, u, d, eps);
+  else hipLaunchKernelGGL((layernorm_kernel<T, 32>), grid, block, 0, s, x, g, b, u, d, eps);
+}
+
+template <int EPI>
+void launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
+  const int64_t big = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+  if (big >= 256) {
+    const unsigned grid = unsigned(big);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, EPI>), dim3(grid), dim3(256), 0, s, g);
+  } else {
+    const unsigned grid = unsigned(((g.M + 127) / 128) * ((g.N + 127) / 128));
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, EPI>), dim3(grid), dim3(256), 0, s, g);
+  }
+}
+
+template <int EPI>
+void launch_gemm_f32(const GemmArgsF32& g, hipStream_t s) {
+  const unsigned grid = unsigned(((g.M + 63) / 64) * ((g.N + 63) / 64));
+  hipLaunchKernelGGL((gemm_f32_kernel<EPI>), dim3(grid), dim3(256), 0, s, g);
+}
+
+void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, int B, int S, int H, int hd, int W,
+                      int dtype, hipStream_t s) {
+  const float scale = 1.0f / std::sqrt(float(hd));
+  if (dtype == PBLOCK_BF16) {
+    AttnArgs a;
+    a.qkv = static_cast<const uint16_t*>(qkv);
+    a.ld_qkv = ld_qkv;
+    a.o = static_cast<uint16_t*>(o);
+    a.ld_o = ld_o;
+    a.B = B; a.S = S; a.H = H; a.W = W;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const unsigned grid = unsigned(((S + kAttnBQ - 1) / kAttnBQ) * int64_t(B) * H);
+    if (hd == 128) hipLaunchKernelGGL((swa_attn_bf16_kernel<128>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((swa_attn_bf16_kernel<64>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    const dim3 grid{unsigned(int64_t((S + 63) / 64) * H * B)};
+    const float* q = static_cast<const float*>(qkv);
+    float* out = static_cast<float*>(o);
+    if (hd == 128) hipLaunchKernelGGL((swa_attn_f32_kernel<128>), grid, dim3(64), 0, s, q, ld_qkv, out, ld_o, S, H, W, scale);
+    else hipLaunchKernelGGL((swa_attn_f32_kernel<64>), grid, dim3(64), 0, s, q, ld_qkv, out, ld_o, S, H, W, scale);
+  }
+}
+
+constexpr int kTimedKernels = 4;
+constexpr size_t kEventPool = 256;
+
+}  // namespace
+
+struct pblock_s {
+  pblock_cfg cfg;
+  int device;
+  int64_t m_cap;
+  int64_t last_m;  // B*S of the most recent forward (0: none yet)
+  void* ws;
+  WsLayout lay;
+  bool timing;
+  std::vector<std::array<hipEvent_t, kTimedKernels + 1>> events;
+  size_t ev_used;
+  double ms_sum[kTimedKernels];
+  int n_forwards;
+};
+
+namespace {
+
+void destroy_events(pblock_s* h) {
+  for (auto& set : h->events)
+    for (auto e : set) (void)hipEventDestroy(e);
+  h->events.clear();
+  h->ev_used = 0;
+}
+
+int drain_events(pblock_s* h) {
+  for (size_t i = 0; i < h->ev_used; ++i) {
+    auto& set = h->events[i];
+    hipError_t e = hipEventSynchronize(set[kTimedKernels]);
+    if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
+    for (int k = 0; k < kTimedKernels; ++k) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, set[k], set[k + 1]);
+      if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipEventElapsedTime: ") + hipGetErrorString(e));
+      h->ms_sum[k] += ms;
+    }
+    h->n_forwards += 1;
+  }
+  h->ev_used = 0;
+  return PBLOCK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pblock_validate_cfg(const pblock_cfg* cfg) {
+  try {
+    return validate(cfg);
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int64_t pblock_workspace_bytes(const pblock_cfg* cfg) {
+  const int st = validate(cfg);
+  if (st != PBLOCK_OK) return st;
+  return ws_layout(cfg).total;
+}
+
+double pblock_flops(const pblock_cfg* cfg) {
+  if (validate(cfg) != PBLOCK_OK) return -1.0;
+  const Dims dm = dims(cfg);
+  const int64_t S = cfg->S, w = std::min<int64_t>(cfg->W, cfg->S);
+  const double keys = double(S * w - w * (w - 1) / 2);
+  return 2.0 * dm.M * cfg->d * dm.n_in + 2.0 * dm.M * dm.k_out * cfg->d + 4.0 * cfg->B * cfg->H * cfg->hd * keys;
+}
+
+int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle) {
+  try {
+    if (!out_handle) return fail(PBLOCK_ERR_NULL, "out_handle is NULL");
+    int st = validate(cfg);
+    if (st != PBLOCK_OK) return st;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st != PBLOCK_OK) return st;
+    pblock_s* h = new pblock_s();
+    h->cfg = *cfg;
+    h->device = dev;
+    h->m_cap = int64_t(cfg->B) * cfg->S;
+    h->last_m = 0;
+    h->lay = ws_layout(cfg);
+    h->ws = nullptr;
+    h->timing = false;
+    h->ev_used = 0;
+    h->n_forwards = 0;
+    for (double& v : h->ms_sum) v = 0.0;
+    hipError_t e = hipMalloc(&h->ws, size_t(h->lay.total));
+    if (e != hipSuccess) {
+      delete h;
+      (void)hipGetLastError();
+      return fail(PBLOCK_ERR_NOMEM, std::string("hipMalloc workspace: ") + hipGetErrorString(e));
+    }
+    *out_handle = h;
+    return PBLOCK_OK;
+  } catch (...) {
+    return fail(PBLOCK_ERR_NOMEM, "host allocation failed");
+  }
+}
+
+int pblock_destroy(pblock_t h) {
+  if (!h) return PBLOCK_OK;
+  destroy_events(h);
+  hipError_t e = hipFree(h->ws);
+  delete h;
+  if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipFree: ") + hipGetErrorString(e));
+  return PBLOCK_OK;
+}
+
+int pblock_intermediates(pblock_t h, void** u, void** qkv, void** ag) {
+  if (!h) return fail(PBLOCK_ERR_NULL, "handle is NULL");
+  char* base = static_cast<char*>(h->ws);
+  if (u) *u = base + h->lay.u;
+  if (qkv) *qkv = base + h->lay.qkv;
+  if (ag) *ag = base + h->lay.ag;
+  return PBLOCK_OK;
+}
+
+int pblock_copy_intermediates(pblock_t h, void* u, void* qkv, void* ag, void* stream) {
+  if (!h) return fail(PBLOCK_ERR_NULL, "handle is NULL");
+  if (h->last_m == 0) return fail(PBLOCK_ERR_ARG, "no forward has run on this handle");
+  const Dims dm = dims(&h->cfg);
+  const int64_t es = elem_size(h->cfg.dtype), M = h->last_m;
+  const char* base = static_cast<const char*>(h->ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  struct Item { void* dst; int64_t off, bytes; } items[3] = {
+      {u, h->lay.u, M * h->cfg.d * es}, {qkv, h->lay.qkv, M * 3 * dm.A * es}, {ag, h->lay.ag, M * dm.k_out * es}};
+  for (const Item& it : items) {
+    if (!it.dst) continue;
+    hipError_t e = hipMemcpyAsync(it.dst, base + it.off, size_t(it.bytes), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
+  }
+  return PBLOCK_OK;
+}
+
+int pblock_set_timing(pblock_t h, int enable) {
+  try {
+    if (!h) return fail(PBLOCK_ERR_NULL, "handle is NULL");
+    destroy_events(h);
+    for (double& v : h->ms_sum) v = 0.0;
+    h->n_forwards = 0;
+    h->timing = enable != 0;
+    if (h->timing) {
+      h->events.resize(kEventPool);
+      for (auto& set : h->events)
+        for (auto& ev : set) {
+          hipError_t e = hipEventCreate(&ev);
+          if (e != hipSuccess) {
+            h->timing = false;
+            return fail(PBLOCK_ERR_HIP, std::string("hipEventCreate: ") + hipGetErrorString(e));
+          }
+        }
+    }
+    return PBLOCK_OK;
+  } catch (...) {
+    return fail(PBLOCK_ERR_NOMEM, "host allocation failed");
+  }
+}
+
+int pblock_kernel_times(pblock_t h, float* ms, int n, int* n_forwards) {
+  if (!h || !ms) return fail(PBLOCK_ERR_NULL, "handle or ms is NULL");
+  if (n < kTimedKernels) return fail(PBLOCK_ERR_ARG, "n must be >= 4");
+  int st = drain_events(h);
+  if (st != PBLOCK_OK) return st;
+  for (int k = 0; k < kTimedKernels; ++k) ms[k] = float(h->ms_sum[k]);
+  if (n_forwards) *n_forwards = h->n_forwards;
+  return PBLOCK_OK;
+}
+
+int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out,
+                   void* stream) {
+  try {
+    if (!h) return fail(PBLOCK_ERR_NULL, "handle is NULL");
+    if (!x || !w || !out || !w->ln_gamma || !w->ln_beta || !w->w_in || !w->w_out)
+      return fail(PBLOCK_ERR_NULL, "x, out, weights or a weight pointer is NULL");
+    int st = validate(cfg);
+    if (st != PBLOCK_OK) return st;
+    const pblock_cfg& c = *cfg;
+    const pblock_cfg& hc = h->cfg;
+    if (c.d != hc.d || c.H != hc.H || c.hd != hc.hd || c.ffn != hc.ffn || c.dtype != hc.dtype)
+      return fail(PBLOCK_ERR_CFG_MISMATCH, "d, H, hd, ffn and dtype must equal the handle's");
+    const Dims dm = dims(&c);
+    if (dm.M > h->m_cap) return fail(PBLOCK_ERR_CFG_MISMATCH, "B*S exceeds the handle's B*S");
+    if (!aligned16(x) || !aligned16(out) || !aligned16(w->ln_gamma) || !aligned16(w->ln_beta) ||
+        !aligned16(w->w_in) || !aligned16(w->w_out))
+      return fail(PBLOCK_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const int es = elem_size(c.dtype);
+    const int64_t xb = dm.M * c.d * es;
+    if (overlap(out, xb, x, xb) || overlap(out, xb, w->w_in, dm.n_in * c.d * es) ||
+        overlap(out, xb, w->w_out, int64_t(c.d) * dm.k_out * es) || overlap(out, xb, w->ln_gamma, c.d * es) ||
+        overlap(out, xb, w->ln_beta, c.d * es))
+      return fail(PBLOCK_ERR_ALIAS, "out overlaps x or a weight");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev != h->device) return fail(PBLOCK_ERR_DEVICE, "current device differs from the handle's");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(h->ws);
+    void* u = base + h->lay.u;
+    void* qkv = base + h->lay.qkv;
+    void* ag = base + h->lay.ag;
+
+    std::array<hipEvent_t, kTimedKernels + 1>* ev = nullptr;
+    if (h->timing) {
+      if (h->ev_used == h->events.size()) {
+        st = drain_events(h);
+        if (st != PBLOCK_OK) return st;
+      }
+      ev = &h->events[h->ev_used++];
+      (void)hipEventRecord((*ev)[0], s);
+    }
+
+    if (c.dtype == PBLOCK_BF16) {
+      launch_layernorm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->ln_gamma),
+                       static_cast<const uint16_t*>(w->ln_beta), static_cast<uint16_t*>(u), dm.M, c.d, c.ln_eps, s);
+    } else {
+      launch_layernorm(static_cast<const float*>(x), static_cast<const float*>(w->ln_gamma),
+                       static_cast<const float*>(w->ln_beta), static_cast<float*>(u), dm.M, c.d, c.ln_eps, s);
+    }
+    if (ev) (void)hipEventRecord((*ev)[1], s);
+
+    if (c.dtype == PBLOCK_BF16) {
+      GemmArgs g{};
+      g.a = static_cast<const uint16_t*>(u); g.lda = c.d;
+      g.b = static_cast<const uint16_t*>(w->w_in); g.ldb = c.d;
+      g.M = int(dm.M); g.N = int(dm.n_in); g.K = c.d;
+      g.out0 = static_cast<uint16_t*>(qkv); g.ld0 = 3 * dm.A;
+      g.out1 = static_cast<uint16_t*>(ag); g.ld1 = dm.k_out; g.off1 = dm.A;
+      g.nsplit = int(3 * dm.A);
+      launch_gemm_bf16<kEpiSplitGelu>(g, s);
+    } else {
+      GemmArgsF32 g{};
+      g.a = static_cast<const float*>(u); g.lda = c.d;
+      g.b = static_cast<const float*>(w->w_in); g.ldb = c.d;
+      g.M = int(dm.M); g.N = int(dm.n_in); g.K = c.d;
+      g.out0 = static_cast<float*>(qkv); g.ld0 = 3 * dm.A;
+      g.out1 = static_cast<float*>(ag); g.ld1 = dm.k_out; g.off1 = dm.A;
+      g.nsplit = int(3 * dm.A);
+      launch_gemm_f32<kEpiSplitGelu>(g, s);
+    }
+    if (ev) (void)hipEventRecord((*ev)[2], s);
+
+    launch_attention(qkv, 3 * dm.A, ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
+    if (ev) (void)hipEventRecord((*ev)[3], s);
+
+    if (c.dtype == PBLOCK_BF16) {
+      GemmArgs g{};
+      g.a = static_cast<const uint16_t*>(ag); g.lda = dm.k_out;
+      g.b = static_cast<const uint16_t*>(w->w_out); g.ldb = dm.k_out;
+      g.M = int(dm.M); g.N = c.d; g.K = int(dm.k_out);
+      g.out0 = static_cast<uint16_t*>(out); g.ld0 = c.d;
+      g.resid = c.add_residual ? static_cast<const uint16_t*>(x) : nullptr; g.ldr = c.d;
+      launch_gemm_bf16<kEpiResidual>(g, s);
+    } else {
+      GemmArgsF32 g{};
+      g.a = static_cast<const float*>(ag); g.lda = dm.k_out;
+      g.b = static_cast<const float*>(w->w_out); g.ldb = dm.k_out;
+      g.M = int(dm.M); g.N = c.d; g.K = int(dm.k_out);
+      g.out0 = static_cast<float*>(out); g.ld0 = c.d;
+      g.resid = c.add_residual ? static_cast<const float*>(x) : nullptr; g.ldr = c.d;
+      launch_gemm_f32<kEpiResidual>(g, s);
+    }
+    if (ev) (void)hipEventRecord((*ev)[4], s);
+    h->last_m = dm.M;
+    return launch_status("pblock_forward launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int pblock_swa_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, int32_t B, int32_t S, int32_t H,
+                         int32_t hd, int32_t W, int32_t dtype, void* stream) {
+  try {
+    if (!qkv || !o) return fail(PBLOCK_ERR_NULL, "qkv or o is NULL");
+    if (dtype != PBLOCK_F32 && dtype != PBLOCK_BF16) return fail(PBLOCK_ERR_DTYPE, "dtype must be F32 or BF16");
+    if (B < 1 || S < 1 || H < 1 || W < 1 || int64_t(B) * S > (int64_t(1) << 24) || H > 4096)
+      return fail(PBLOCK_ERR_SHAPE, "B, S, H, W must be >= 1 (B*S <= 2^24, H <= 4096)");
+    if (hd != 64 && hd != 128) return fail(PBLOCK_ERR_SHAPE, "hd must be 64 or 128");
+    const int64_t A = int64_t(H) * hd;
+    if (ld_qkv < 3 * A || ld_o < A || (ld_qkv % 8) != 0 || (ld_o % 8) != 0)
+      return fail(PBLOCK_ERR_SHAPE, "ld_qkv >= 3*H*hd and ld_o >= H*hd, both multiples of 8");
+    if (!aligned16(qkv) || !aligned16(o)) return fail(PBLOCK_ERR_ALIGN, "qkv and o must be 16-byte aligned");
+    const int es = elem_size(dtype);
+    const int64_t M = int64_t(B) * S;
+    if (overlap(qkv, ((M - 1) * ld_qkv + 3 * A) * es, o, ((M - 1) * ld_o + A) * es))
+      return fail(PBLOCK_ERR_ALIAS, "o overlaps qkv");
+    int st = check_device(nullptr);
+    if (st != PBLOCK_OK) return st;
+    launch_attention(qkv, ld_qkv, o, ld_o, B, S, H, hd, W, dtype, static_cast<hipStream_t>(stream));
+    return launch_status("pblock_swa_attention launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+const char* pblock_strerror(int code) {
+  switch (code) {
+    case PBLOCK_OK: return "ok";
+    case PBLOCK_ERR_NULL: return "a required pointer is NULL";
+    case PBLOCK_ERR_SHAPE: return "a dimension is out of the supported range";
+    case PBLOCK_ERR_DTYPE: return "unsupported dtype";
+    case PBLOCK_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case PBLOCK_ERR_ALIAS: return "output overlaps an input";
+    case PBLOCK_ERR_CFG_MISMATCH: return "cfg does not match the handle";
+    case PBLOCK_ERR_DEVICE: return "no gfx950 device is current";
+    case PBLOCK_ERR_NOMEM: return "out of memory";
+    case PBLOCK_ERR_HIP: return "HIP runtime error";
+    case PBLOCK_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* pblock_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
