@@ -121,22 +121,28 @@ def test_large_config_sampled(name):
 
 
 def test_branch_sum_on_gpu():
-    """y - x == attention branch alone (FC1 rows zero) + MLP branch alone (V rows zero)."""
+    """Branch sum (the full block without residual) == attention branch alone
+    (FC1 rows zero, GeLU(0) = 0) + MLP branch alone (V rows zero).  All three
+    are emitted without the residual so each is rounded to bf16 at the scale
+    of the branches, not at the scale of x."""
     cfg = BlockConfig("branches", B=2, S=160, d=256, H=2, hd=128, ffn=384, W=40, dtype="bf16")
     inp = make_inputs(cfg, seed=5, affine=True)
     dev = upload(inp)
     A = cfg.A
-    y_full = run_block(cfg, dev)
     part = cfg.replace(add_residual=0)
+    y_full = run_block(part, dev)
+    y_res = run_block(cfg, dev)
     w_attn = dev["w_in"].clone()
     w_attn[3 * A:] = 0
     w_mlp = dev["w_in"].clone()
     w_mlp[2 * A:3 * A] = 0
     y_attn = run_block(part, {**dev, "w_in": w_attn})
     y_mlp = run_block(part, {**dev, "w_in": w_mlp})
-    err = rel_err(y_attn + y_mlp, y_full - inp.x)
+    err = rel_err(y_attn + y_mlp, y_full)
     log(f"[parity] branch sum: {err:.3e}")
     assert err <= TOL["bf16"]
+    # and the residual variant is the partial plus x, to bf16 rounding of the sum
+    assert np.abs(y_res - (y_full + inp.x)).max() <= 2 ** -7 * np.abs(y_res).max()
     assert np.abs(y_attn).max() > 1e-3 and np.abs(y_mlp).max() > 1e-3
 
 
@@ -264,19 +270,34 @@ def test_deterministic_and_reusable_handle():
 
 
 def test_errors_leave_output_untouched():
+    """Rejected calls (through the raw C ABI, past the binding's own checks)
+    enqueue nothing: the output keeps its sentinel."""
+    import ctypes
+
     cfg = BlockConfig("err", B=1, S=64, d=128, H=1, hd=64, ffn=64, W=8, dtype="bf16")
     inp = make_inputs(cfg, seed=13)
     dev = upload(inp)
+    lib = tb._abi.lib()
     h = tb.pblock_create(cfg)
     try:
         out = torch.full_like(dev["x"], 7.0)
-        w = (dev["gamma"], dev["beta"], dev["w_in"], dev["w_out"])
-        with pytest.raises(tb.PblockError) as ei:
-            tb.pblock_forward(h, dev["x"], w, cfg.replace(d=192), out)
-        assert ei.value.code == tb._abi.PBLOCK_ERR_CFG_MISMATCH
-        with pytest.raises(tb.PblockError) as ei:
-            tb.pblock_forward(h, dev["x"], w, cfg, dev["x"])
-        assert ei.value.code == tb._abi.PBLOCK_ERR_ALIAS
+        w = tb.PblockWeights(dev["gamma"].data_ptr(), dev["beta"].data_ptr(), dev["w_in"].data_ptr(),
+                             dev["w_out"].data_ptr())
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def call(c, x_ptr, out_ptr, weights=w):
+            return lib.pblock_forward(ctypes.c_void_p(h), x_ptr, ctypes.byref(weights), ctypes.byref(tb.as_cfg(c)),
+                                      out_ptr, stream)
+
+        x_ptr, o_ptr = dev["x"].data_ptr(), out.data_ptr()
+        assert call(cfg.replace(d=192), x_ptr, o_ptr) == tb._abi.PBLOCK_ERR_CFG_MISMATCH
+        assert call(cfg.replace(S=65), x_ptr, o_ptr) == tb._abi.PBLOCK_ERR_CFG_MISMATCH
+        assert call(cfg.replace(hd=96), x_ptr, o_ptr) == tb._abi.PBLOCK_ERR_SHAPE
+        assert call(cfg, x_ptr, x_ptr) == tb._abi.PBLOCK_ERR_ALIAS
+        assert call(cfg, x_ptr + 2, o_ptr) == tb._abi.PBLOCK_ERR_ALIGN
+        assert call(cfg, 0, o_ptr) == tb._abi.PBLOCK_ERR_NULL
+        bad_w = tb.PblockWeights(w.ln_gamma, w.ln_beta, 0, w.w_out)
+        assert call(cfg, x_ptr, o_ptr, bad_w) == tb._abi.PBLOCK_ERR_NULL
         torch.cuda.synchronize()
         assert bool((out == 7.0).all())
     finally:
