@@ -89,8 +89,11 @@ typedef struct pblock_s* pblock_t;
 /* Validates cfg (host only, touches no device).  Returns 0 or an error. */
 int pblock_validate_cfg(const pblock_cfg* cfg);
 
-/* Bytes of device workspace a handle for cfg allocates (u, QKV, AG buffers),
- * or a negative status.  Host only. */
+/* Bytes of device workspace a handle for cfg allocates, or a negative status.
+ * Host only.  The workspace holds the intermediates u, QKV, AG and, for bf16,
+ * the GEMM scratch: two fp32 256x256 partial tiles per persistent workgroup
+ * (one per compute unit; this estimate assumes 256) and one arrival counter
+ * per 256x256 output tile. */
 int64_t pblock_workspace_bytes(const pblock_cfg* cfg);
 
 /* Algorithmic FLOPs of one forward for cfg: 2*M*d*(3*H*hd+ffn) +

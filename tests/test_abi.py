@@ -75,7 +75,13 @@ def test_workspace_and_flops():
         es = 2 if cfg.dtype == "bf16" else 4
         ws = tb.pblock_workspace_bytes(cfg)
         need = es * cfg.M * (cfg.d + 3 * cfg.A + cfg.k_out)
-        assert need <= ws <= need + 3 * 256
+        slack = 5 * 256
+        if cfg.dtype == "bf16":
+            # GEMM scratch (host estimate at 256 CUs): two fp32 256x256 partial tiles per
+            # workgroup plus one arrival counter per output tile
+            tiles = max(-(-cfg.M // 256) * -(-cfg.n_in // 256), -(-cfg.M // 256) * -(-cfg.d // 256))
+            need += 2 * 256 * 256 * 256 * 4 + 4 * tiles
+        assert need <= ws <= need + slack
         assert tb.pblock_flops(cfg) == pytest.approx(cfg.flops(), rel=1e-12)
     bad = tb.as_cfg(CONFIGS["small"])
     bad.hd = 3

@@ -69,17 +69,30 @@ Dims dims(const pblock_cfg* c) {
 
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
+int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + kGemmBM - 1) / kGemmBM) * ((N + kGemmBN - 1) / kGemmBN); }
+
 struct WsLayout {
-  int64_t u, qkv, ag, total;
+  int64_t u, qkv, ag, partials, counters, total;
+  int64_t max_tiles;
 };
-WsLayout ws_layout(const pblock_cfg* c) {
+// G = persistent GEMM workgroups (the device's CU count); 0 for a host-only estimate at 256.
+WsLayout ws_layout(const pblock_cfg* c, int G) {
   const Dims dm = dims(c);
   const int es = elem_size(c->dtype);
+  if (G <= 0) G = 256;
   WsLayout w;
   w.u = 0;
   w.qkv = align256(dm.M * c->d * es);
   w.ag = w.qkv + align256(dm.M * 3 * dm.A * es);
-  w.total = w.ag + align256(dm.M * dm.k_out * es);
+  w.partials = w.ag + align256(dm.M * dm.k_out * es);
+  w.max_tiles = 0;
+  int64_t part_bytes = 0;
+  if (c->dtype == PBLOCK_BF16) {
+    part_bytes = int64_t(2) * G * kGemmBM * kGemmBN * 4;
+    w.max_tiles = std::max(gemm_tiles(dm.M, dm.n_in), gemm_tiles(dm.M, c->d));
+  }
+  w.counters = w.partials + align256(part_bytes);
+  w.total = w.counters + align256(w.max_tiles * 4);
   return w;
 }
 
@@ -130,16 +143,28 @@ void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d
   else hipLaunchKernelGGL((layernorm_kernel<T, 32>), grid, block, 0, s, x, g, b, u, d, eps);
 }
 
+// Stream-K scratch: fp32 partial tiles (two slots per persistent workgroup) and
+// one arrival counter per output tile.
+struct SkScratch {
+  float* partials;
+  int* counters;
+  int G;           // persistent workgroups (one per CU)
+  int64_t max_tiles;
+};
+
 template <int EPI>
-void launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
-  const int64_t big = ((g.M + 255) / 256) * ((g.N + 255) / 256);
-  if (big >= 256) {
-    const unsigned grid = unsigned(big);
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, EPI>), dim3(grid), dim3(256), 0, s, g);
-  } else {
-    const unsigned grid = unsigned(((g.M + 127) / 128) * ((g.N + 127) / 128));
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, EPI>), dim3(grid), dim3(256), 0, s, g);
-  }
+void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s) {
+  StreamK sk;
+  sk.partials = scr.partials;
+  sk.counters = scr.counters;
+  sk.tiles_m = int((g.M + kGemmBM - 1) / kGemmBM);
+  const int64_t tiles = gemm_tiles(g.M, g.N);
+  sk.KT = g.K / kGemmBK;
+  sk.iters = tiles * sk.KT;
+  // at least kMinShare k-slabs per workgroup, so small problems are not split many ways
+  constexpr int64_t kMinShare = 8;
+  sk.G = int(std::max<int64_t>(1, std::min<int64_t>(scr.G, (sk.iters + kMinShare - 1) / kMinShare)));
+  hipLaunchKernelGGL((gemm_bf16_sk_kernel<EPI>), dim3(unsigned(sk.G)), dim3(kGemmThreads), 0, s, g, sk);
 }
 
 template <int EPI>
@@ -181,6 +206,7 @@ struct pblock_s {
   int device;
   int64_t m_cap;
   int64_t last_m;  // B*S of the most recent forward (0: none yet)
+  int n_cu;        // compute units: persistent GEMM workgroups
   void* ws;
   WsLayout lay;
   bool timing;
@@ -231,7 +257,7 @@ int pblock_validate_cfg(const pblock_cfg* cfg) {
 int64_t pblock_workspace_bytes(const pblock_cfg* cfg) {
   const int st = validate(cfg);
   if (st != PBLOCK_OK) return st;
-  return ws_layout(cfg).total;
+  return ws_layout(cfg, 0).total;
 }
 
 double pblock_flops(const pblock_cfg* cfg) {
@@ -255,7 +281,14 @@ int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle) {
     h->device = dev;
     h->m_cap = int64_t(cfg->B) * cfg->S;
     h->last_m = 0;
-    h->lay = ws_layout(cfg);
+    int n_cu = 0;
+    hipError_t ea = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (ea != hipSuccess || n_cu <= 0) {
+      delete h;
+      return fail(PBLOCK_ERR_DEVICE, "cannot query the compute-unit count");
+    }
+    h->n_cu = n_cu;
+    h->lay = ws_layout(cfg, n_cu);
     h->ws = nullptr;
     h->timing = false;
     h->ev_used = 0;
@@ -266,6 +299,13 @@ int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle) {
       delete h;
       (void)hipGetLastError();
       return fail(PBLOCK_ERR_NOMEM, std::string("hipMalloc workspace: ") + hipGetErrorString(e));
+    }
+    // stream-K arrival counters start at zero; every launch leaves them at zero
+    e = hipMemset(static_cast<char*>(h->ws) + h->lay.counters, 0, size_t(h->lay.total - h->lay.counters));
+    if (e != hipSuccess) {
+      (void)hipFree(h->ws);
+      delete h;
+      return fail(PBLOCK_ERR_HIP, std::string("hipMemset counters: ") + hipGetErrorString(e));
     }
     *out_handle = h;
     return PBLOCK_OK;
@@ -375,6 +415,11 @@ int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pbl
     void* u = base + h->lay.u;
     void* qkv = base + h->lay.qkv;
     void* ag = base + h->lay.ag;
+    SkScratch scr;
+    scr.partials = reinterpret_cast<float*>(base + h->lay.partials);
+    scr.counters = reinterpret_cast<int*>(base + h->lay.counters);
+    scr.G = h->n_cu;
+    scr.max_tiles = h->lay.max_tiles;
 
     std::array<hipEvent_t, kTimedKernels + 1>* ev = nullptr;
     if (h->timing) {
@@ -403,7 +448,7 @@ int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pbl
       g.out0 = static_cast<uint16_t*>(qkv); g.ld0 = 3 * dm.A;
       g.out1 = static_cast<uint16_t*>(ag); g.ld1 = dm.k_out; g.off1 = dm.A;
       g.nsplit = int(3 * dm.A);
-      launch_gemm_bf16<kEpiSplitGelu>(g, s);
+      launch_gemm_bf16<kEpiSplitGelu>(g, scr, s);
     } else {
       GemmArgsF32 g{};
       g.a = static_cast<const float*>(u); g.lda = c.d;
@@ -426,7 +471,7 @@ int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pbl
       g.M = int(dm.M); g.N = c.d; g.K = int(dm.k_out);
       g.out0 = static_cast<uint16_t*>(out); g.ld0 = c.d;
       g.resid = c.add_residual ? static_cast<const uint16_t*>(x) : nullptr; g.ldr = c.d;
-      launch_gemm_bf16<kEpiResidual>(g, s);
+      launch_gemm_bf16<kEpiResidual>(g, scr, s);
     } else {
       GemmArgsF32 g{};
       g.a = static_cast<const float*>(ag); g.lda = dm.k_out;
