@@ -14,16 +14,21 @@
 // same logical chunk) hit distinct LDS banks.  Rows past M or N fall outside
 // the buffer descriptor's range and read as zero.
 //
-// Schedule: persistent stream-K.  The (tile, k-slab) iteration space is cut
-// into one equal contiguous share per workgroup (one workgroup per CU), so
-// every CU does the same number of MFMAs whatever the tile count -- no
-// partial last wave.  A tile whose k range is split between workgroups is
-// finished by the last contributor to arrive (per-tile atomic counter, no
-// waiting): contributors store fp32 partials, and the finisher sums all of
-// them in contributor order (bitwise deterministic), applies the epilogue
-// and resets the counter for the next launch.  Workgroup ids are remapped so
-// that each XCD (id mod 8) owns a contiguous run of iterations: tiles that
-// share a weight stripe (M sweeps fastest) sit on the same XCD's L2.
+// Schedule: data-parallel waves plus a split-K tail.  With G workgroups
+// resident at once (one per CU), the first floor(T / G) * G tiles run whole,
+// one workgroup each, in k-lockstep.  The remaining T mod G tiles would fill
+// only part of a last wave, so each is cut into `split` k-chunks (split =
+// G / tail) and the chunks run together as one more wave: every CU gets
+// nearly the same number of MFMAs whatever the tile count.  A chunk stores
+// its fp32 partial; the last chunk to arrive (per-tile atomic counter, no
+// waiting) sums all of them in chunk order (bitwise deterministic), applies
+// the epilogue and resets the counter for the next launch.
+//
+// L2 locality: workgroup ids are remapped so each XCD (id mod 8) owns a
+// contiguous run of work units, and units are ordered in groups of 8 M-tiles
+// (M fastest): the 32 workgroups an XCD runs at once cover an 8 (M) x 4 (N)
+// block of tiles at the same k, so they share activation and weight slabs in
+// that XCD's L2.
 //
 // Epilogues:
 //   kEpiSplitGelu: columns < nsplit are stored as bf16 to out0 (the Q|K|V
@@ -56,28 +61,40 @@ struct GemmArgs {
 constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 64;
 constexpr int kGemmThreads = 512;
 
-struct StreamK {
-  float* partials;  // [2 * G][kGemmBM * kGemmBN] fp32 (slot, then float4 row, then thread)
-  int* counters;    // [tiles], zero between launches
-  int tiles_m;
+// Work decomposition of one GEMM launch (grid = dp_units + tail * split).
+struct GemmSched {
+  float* partials;  // [tail * split][kGemmBM * kGemmBN] fp32 (chunk slot, then float4 row, then thread)
+  int* counters;    // [tail], zero between launches
+  int tiles_m, tiles_n;
   int KT;           // k slabs per tile
-  int64_t iters;    // tiles * KT
-  int G;            // persistent workgroups (== gridDim.x)
+  int dp_units;     // tiles computed whole (a multiple of the resident workgroup count)
+  int tail;         // tiles computed in k-chunks
+  int split;        // k-chunks per tail tile
 };
 
-// Iteration-space share of (virtual) workgroup g: [sk_start(g), sk_start(g + 1)).
-__device__ __forceinline__ int64_t sk_start(int g, int64_t iters, int G) { return (int64_t(g) * iters) / G; }
+constexpr int kGroupM = 8;
 
-__device__ __forceinline__ int xcd_remap(int bid, int G) {
+// Contiguous-per-XCD renumbering of workgroup ids 0 .. n-1 (id mod 8 picks the XCD).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int xcd = bid & 7, idx = bid >> 3;
-  const int per = G >> 3, rem = G & 7;
+  const int per = n >> 3, rem = n & 7;
   return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+// Tile coordinates of linear tile index L: groups of kGroupM M-tiles, M fastest.
+__device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int group = kGroupM * tiles_n;
+  const int first_m = (L / group) * kGroupM;
+  const int gsz = min(tiles_m - first_m, kGroupM);
+  const int r = L % group;
+  *tm = first_m + r % gsz;
+  *tn = r / gsz;
 }
 
 #define PBLK_LDS __attribute__((address_space(3)))
 
 template <int EPI>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_sk_kernel(GemmArgs g, StreamK sk) {
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, GemmSched sk) {
   constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
   constexpr int WN = 4;
   constexpr int TM = 128, TN = 64;
@@ -90,9 +107,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_sk_kernel(GemmArgs 
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lg = lane >> 5;
-  const int G = sk.G;
-  const int vg = xcd_remap(blockIdx.x, G);
-
   // DMA lane geometry: lane l of a 1 KiB block fills LDS row l/8 of the block,
   // physical chunk l%8, which holds logical chunk (l%8) ^ (l/8) of that row.
   const int dma_row = lane >> 3;
@@ -102,15 +116,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_sk_kernel(GemmArgs 
   const int b_row0 = wn * TN + lr;
   const int swz = lr & 7;
 
-  int64_t it = sk_start(vg, sk.iters, G);
-  const int64_t it_end = sk_start(vg + 1, sk.iters, G);
-
-  while (it < it_end) {
-    const int t = int(it / sk.KT);
-    const int kb = int(it - int64_t(t) * sk.KT);
-    const int ke = int(min<int64_t>(sk.KT, kb + (it_end - it)));
-    const int m0 = (t % sk.tiles_m) * BM;
-    const int n0 = (t / sk.tiles_m) * BN;
+  // this workgroup's unit: a whole tile, or k-chunk `chunk` of tail tile `tl`
+  int L, kb, ke, tl = -1, chunk = 0;
+  if (int(blockIdx.x) < sk.dp_units) {
+    L = xcd_remap(blockIdx.x, sk.dp_units);
+    kb = 0;
+    ke = sk.KT;
+  } else {
+    const int nu = sk.tail * sk.split;
+    const int u = xcd_remap(blockIdx.x - sk.dp_units, nu);
+    chunk = u / sk.tail;
+    tl = u % sk.tail;
+    L = sk.dp_units + tl;
+    kb = int((int64_t(chunk) * sk.KT) / sk.split);
+    ke = int((int64_t(chunk + 1) * sk.KT) / sk.split);
+  }
+  int tm, tn;
+  tile_coords(L, sk.tiles_m, sk.tiles_n, &tm, &tn);
+  {
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
 
     // buffer descriptors anchored at the tile's first row; rows past the end read as zero
     const uint16_t* a_base = g.a + int64_t(m0) * g.lda;
@@ -171,25 +196,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_sk_kernel(GemmArgs 
       __syncthreads();
     }
 
-    bool finish = (kb == 0 && ke == sk.KT);
+    bool finish = (tl < 0);
     if (!finish) {
-      // contributors of tile t: the workgroups whose shares intersect [t*KT, (t+1)*KT)
-      const int64_t t0 = int64_t(t) * sk.KT, t1 = t0 + sk.KT;
-      int g_lo = int((t0 * G) / sk.iters);
-      while (g_lo > 0 && sk_start(g_lo, sk.iters, G) > t0) --g_lo;
-      while (sk_start(g_lo + 1, sk.iters, G) <= t0) ++g_lo;
-      int g_hi = int(((t1 - 1) * G) / sk.iters);
-      while (g_hi > 0 && sk_start(g_hi, sk.iters, G) > t1 - 1) --g_hi;
-      while (g_hi + 1 < G && sk_start(g_hi + 1, sk.iters, G) <= t1 - 1) ++g_hi;
-      const int n_contrib = g_hi - g_lo + 1;
-      // A workgroup keeps the partial of the tile its share starts in (its first
-      // segment) in slot 0 and that of the tile its share ends in in slot 1.  Every
-      // contributor after g_lo starts inside t; g_lo starts inside t only if its
-      // share begins exactly at t0.
-      const int lo_slot = 2 * g_lo + (sk_start(g_lo, sk.iters, G) == t0 ? 0 : 1);
-      const int my_slot = (vg == g_lo) ? lo_slot : 2 * vg;
       constexpr int TILE4 = BM * BN / 4;
-      f32x4* mine = reinterpret_cast<f32x4*>(sk.partials) + int64_t(my_slot) * TILE4;
+      f32x4* mine = reinterpret_cast<f32x4*>(sk.partials) + int64_t(tl * sk.split + chunk) * TILE4;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -202,21 +212,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_sk_kernel(GemmArgs 
           }
       __threadfence();
       __syncthreads();
-      if (tid == 0) s_old = atomicAdd(sk.counters + t, 1);
+      if (tid == 0) s_old = atomicAdd(sk.counters + tl, 1);
       __syncthreads();
-      finish = (s_old == n_contrib - 1);
+      finish = (s_old == sk.split - 1);
       if (finish) {
         __threadfence();
-        // sum every contributor's partial (own included) in contributor order:
-        // the result does not depend on which workgroup arrived last
+        // sum every chunk's partial (own included) in chunk order: the result does
+        // not depend on which chunk arrived last
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-        for (int c = g_lo; c <= g_hi; ++c) {
-          const f32x4* p = reinterpret_cast<const f32x4*>(sk.partials) + int64_t(c == g_lo ? lo_slot : 2 * c) * TILE4;
+        for (int c = 0; c < sk.split; ++c) {
+          const f32x4* p = reinterpret_cast<const f32x4*>(sk.partials) + int64_t(tl * sk.split + c) * TILE4;
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_sk_kernel(GemmArgs 
                 acc[i][j][4 * q + 3] += v[3];
               }
         }
-        if (tid == 0) sk.counters[t] = 0;
+        if (tid == 0) sk.counters[tl] = 0;
       }
     }
 
@@ -272,7 +282,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_sk_kernel(GemmArgs 
         }
       }
     }
-    it += (ke - kb);
   }
 }
 

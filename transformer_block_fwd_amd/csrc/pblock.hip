@@ -88,8 +88,9 @@ WsLayout ws_layout(const pblock_cfg* c, int G) {
   w.max_tiles = 0;
   int64_t part_bytes = 0;
   if (c->dtype == PBLOCK_BF16) {
-    part_bytes = int64_t(2) * G * kGemmBM * kGemmBN * 4;
-    w.max_tiles = std::max(gemm_tiles(dm.M, dm.n_in), gemm_tiles(dm.M, c->d));
+    // the split-K tail holds at most G chunks in flight, and fewer than G tiles
+    part_bytes = int64_t(G) * kGemmBM * kGemmBN * 4;
+    w.max_tiles = G;
   }
   w.counters = w.partials + align256(part_bytes);
   w.total = w.counters + align256(w.max_tiles * 4);
@@ -143,28 +144,43 @@ void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d
   else hipLaunchKernelGGL((layernorm_kernel<T, 32>), grid, block, 0, s, x, g, b, u, d, eps);
 }
 
-// Stream-K scratch: fp32 partial tiles (two slots per persistent workgroup) and
-// one arrival counter per output tile.
+// GEMM scratch: fp32 partial tiles of the split-K tail (at most one wave of
+// chunks) and one arrival counter per tail tile.
 struct SkScratch {
   float* partials;
   int* counters;
-  int G;           // persistent workgroups (one per CU)
-  int64_t max_tiles;
+  int G;  // workgroups resident at once (one per CU)
 };
+
+// Split of a T-tile GEMM over G resident workgroups: whole tiles in full waves,
+// the remainder cut into k-chunks so that the last wave is (nearly) full.
+struct Split {
+  int dp_units, tail, split;
+};
+Split plan_split(int64_t T, int KT, int G) {
+  Split p;
+  const int64_t waves = T / G;
+  p.tail = int(T - waves * G);
+  p.dp_units = int(waves * G);
+  p.split = 1;
+  if (p.tail > 0) p.split = int(std::max<int64_t>(1, std::min<int64_t>(G / p.tail, KT)));
+  return p;
+}
 
 template <int EPI>
 void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s) {
-  StreamK sk;
+  GemmSched sk;
   sk.partials = scr.partials;
   sk.counters = scr.counters;
   sk.tiles_m = int((g.M + kGemmBM - 1) / kGemmBM);
-  const int64_t tiles = gemm_tiles(g.M, g.N);
+  sk.tiles_n = int((g.N + kGemmBN - 1) / kGemmBN);
   sk.KT = g.K / kGemmBK;
-  sk.iters = tiles * sk.KT;
-  // at least kMinShare k-slabs per workgroup, so small problems are not split many ways
-  constexpr int64_t kMinShare = 8;
-  sk.G = int(std::max<int64_t>(1, std::min<int64_t>(scr.G, (sk.iters + kMinShare - 1) / kMinShare)));
-  hipLaunchKernelGGL((gemm_bf16_sk_kernel<EPI>), dim3(unsigned(sk.G)), dim3(kGemmThreads), 0, s, g, sk);
+  const Split p = plan_split(int64_t(sk.tiles_m) * sk.tiles_n, sk.KT, scr.G);
+  sk.dp_units = p.dp_units;
+  sk.tail = p.tail;
+  sk.split = p.split;
+  const unsigned grid = unsigned(p.dp_units + p.tail * p.split);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
 }
 
 template <int EPI>
@@ -419,7 +435,6 @@ int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pbl
     scr.partials = reinterpret_cast<float*>(base + h->lay.partials);
     scr.counters = reinterpret_cast<int*>(base + h->lay.counters);
     scr.G = h->n_cu;
-    scr.max_tiles = h->lay.max_tiles;
 
     std::array<hipEvent_t, kTimedKernels + 1>* ev = nullptr;
     if (h->timing) {
