@@ -8,11 +8,11 @@
 // out 2 (M) x 4 (N); each wavefront owns 128 x 64 as 4 x 2 MFMA tiles of
 // 32 x 32 with fp32 accumulators.  The k loop walks 64-wide slabs through two
 // LDS stages (2 x 64 KiB).  Global data moves straight into LDS with
-// buffer_load_dwordx4 ... lds (no staging registers): each instruction fills
+// global_load_lds_dwordx4 (no staging registers): each instruction fills
 // 1 KiB = 8 rows of 128 bytes.  The 16-byte chunk index inside a row is XORed
 // with (row & 7) on the source side, so the fragment reads (8 lanes on 8 rows,
-// same logical chunk) hit distinct LDS banks.  Rows past M or N fall outside
-// the buffer descriptor's range and read as zero.
+// same logical chunk) hit distinct LDS banks.  Rows past M or N are clamped to
+// the last valid row (their results are never stored).
 //
 // Schedule: data-parallel waves plus a split-K tail.  With G workgroups
 // resident at once (one per CU), the first floor(T / G) * G tiles run whole,
@@ -100,7 +100,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   constexpr int TM = 128, TN = 64;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int STAGE = (BM + BN) * BK;  // elements per LDS stage
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+  // two LDS stages as two distinct arrays: the compiler can then tell that the
+  // DMA filling one stage never aliases the fragment reads of the other, and
+  // does not wait for the prefetch before reading the current slab
+  __shared__ __attribute__((aligned(1024))) uint16_t smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem1[STAGE];
   __shared__ int s_old;
 
   const int tid = threadIdx.x;
@@ -137,31 +141,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     const int m0 = tm * BM;
     const int n0 = tn * BN;
 
-    // buffer descriptors anchored at the tile's first row; rows past the end read as zero
-    const uint16_t* a_base = g.a + int64_t(m0) * g.lda;
-    const uint16_t* b_base = g.b + int64_t(n0) * g.ldb;
-    const int64_t a_bytes = int64_t(g.M - m0) * g.lda * 2, b_bytes = int64_t(g.N - n0) * g.ldb * 2;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a_base), 0, int(min<int64_t>(a_bytes, 0x7FFFFFFF)), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(b_base), 0, int(min<int64_t>(b_bytes, 0x7FFFFFFF)), 0x00020000);
-    // wave w fills blocks 4w .. 4w+3 of each operand: tile rows 32w + 8i + l/8
-    const uint32_t a_voff = uint32_t((int64_t(wave * 32 + dma_row) * g.lda + dma_chunk * 8) * 2);
-    const uint32_t b_voff = uint32_t((int64_t(wave * 32 + dma_row) * g.ldb + dma_chunk * 8) * 2);
-    const uint32_t a_step = uint32_t(8 * g.lda * 2), b_step = uint32_t(8 * g.ldb * 2);
+    // per-lane source pointers (rows clamped to the last valid row)
+    const uint16_t* a_src[4];
+    const uint16_t* b_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = min(m0 + wave * 32 + 8 * i + dma_row, g.M - 1);
+      const int rb = min(n0 + wave * 32 + 8 * i + dma_row, g.N - 1);
+      a_src[i] = g.a + int64_t(ra) * g.lda + dma_chunk * 8;
+      b_src[i] = g.b + int64_t(rb) * g.ldb + dma_chunk * 8;
+    }
 
-    auto issue = [&](int kt, int stage) {
-      const uint32_t koff = uint32_t(kt * BK * 2);
-      uint16_t* sa = smem + stage * STAGE + wave * 4 * 512;
-      uint16_t* sb = smem + stage * STAGE + BM * BK + wave * 4 * 512;
+    auto issue = [&](int kt, uint16_t* stage) {
+      const int koff = kt * BK;
+      uint16_t* sa = stage + wave * 4 * 512;
+      uint16_t* sb = stage + BM * BK + wave * 4 * 512;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (PBLK_LDS void*)(sa + i * 512), 16, a_voff + i * a_step, koff,
-                                                 0, 0);
+        __builtin_amdgcn_global_load_lds(a_src[i] + koff, (PBLK_LDS void*)(sa + i * 512), 16, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (PBLK_LDS void*)(sb + i * 512), 16, b_voff + i * b_step, koff,
-                                                 0, 0);
+        __builtin_amdgcn_global_load_lds(b_src[i] + koff, (PBLK_LDS void*)(sb + i * 512), 16, 0, 0);
     };
 
     f32x16 acc[FM][FN];
@@ -172,13 +172,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    issue(kb, 0);
-    __syncthreads();
-    for (int kt = kb; kt < ke; ++kt) {
-      const int cur = (kt - kb) & 1;
-      if (kt + 1 < ke) issue(kt + 1, cur ^ 1);
-      const uint16_t* sa = smem + cur * STAGE;
-      const uint16_t* sb = sa + BM * BK;
+    auto compute = [&](const uint16_t* stage) {
+      const uint16_t* sa = stage;
+      const uint16_t* sb = stage + BM * BK;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         const int ch = ((kk * 2 + lg) ^ swz) << 3;
@@ -192,7 +188,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        // keep the next step's fragment loads from being hoisted here (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+
+    // Slab kb lands in stage 0.  Each pass of the loop handles two slabs, the
+    // first read from stage 0 while the next slab streams into stage 1, the
+    // second the other way round; an odd last slab is read from stage 0.
+    issue(kb, smem0);
+    __syncthreads();
+    int kt = kb;
+    for (; kt + 1 < ke; kt += 2) {
+      issue(kt + 1, smem1);
+      compute(smem0);
+      __syncthreads();
+      if (kt + 2 < ke) issue(kt + 2, smem0);
+      compute(smem1);
+      __syncthreads();
+    }
+    if (kt < ke) {
+      compute(smem0);
       __syncthreads();
     }
 
