@@ -92,7 +92,7 @@ int pblock_validate_cfg(const pblock_cfg* cfg);
 /* Bytes of device workspace a handle for cfg allocates, or a negative status.
  * Host only.  The workspace holds the intermediates u, QKV, AG and, for bf16,
  * the GEMM scratch for the split-K tail wave: one fp32 256x256 partial tile
- * and one arrival counter per compute unit (this estimate assumes 256). */
+ * per compute unit (this estimate assumes 256). */
 int64_t pblock_workspace_bytes(const pblock_cfg* cfg);
 
 /* Algorithmic FLOPs of one forward for cfg: 2*M*d*(3*H*hd+ffn) +

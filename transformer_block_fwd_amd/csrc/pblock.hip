@@ -69,11 +69,9 @@ Dims dims(const pblock_cfg* c) {
 
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
-int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + kGemmBM - 1) / kGemmBM) * ((N + kGemmBN - 1) / kGemmBN); }
 
 struct WsLayout {
-  int64_t u, qkv, ag, partials, counters, total;
-  int64_t max_tiles;
+  int64_t u, qkv, ag, partials, total;
 };
 // G = persistent GEMM workgroups (the device's CU count); 0 for a host-only estimate at 256.
 WsLayout ws_layout(const pblock_cfg* c, int G) {
@@ -85,15 +83,12 @@ WsLayout ws_layout(const pblock_cfg* c, int G) {
   w.qkv = align256(dm.M * c->d * es);
   w.ag = w.qkv + align256(dm.M * 3 * dm.A * es);
   w.partials = w.ag + align256(dm.M * dm.k_out * es);
-  w.max_tiles = 0;
   int64_t part_bytes = 0;
   if (c->dtype == PBLOCK_BF16) {
-    // the split-K tail holds at most G chunks in flight, and fewer than G tiles
+    // the split-K tail holds at most G chunks (one wave)
     part_bytes = int64_t(G) * kGemmBM * kGemmBN * 4;
-    w.max_tiles = G;
   }
-  w.counters = w.partials + align256(part_bytes);
-  w.total = w.counters + align256(w.max_tiles * 4);
+  w.total = w.partials + align256(part_bytes);
   return w;
 }
 
@@ -144,11 +139,9 @@ void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d
   else hipLaunchKernelGGL((layernorm_kernel<T, 32>), grid, block, 0, s, x, g, b, u, d, eps);
 }
 
-// GEMM scratch: fp32 partial tiles of the split-K tail (at most one wave of
-// chunks) and one arrival counter per tail tile.
+// GEMM scratch: fp32 partial tiles of the split-K tail (at most one wave of chunks).
 struct SkScratch {
   float* partials;
-  int* counters;
   int G;  // workgroups resident at once (one per CU)
 };
 
@@ -171,7 +164,6 @@ template <int EPI>
 void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s) {
   GemmSched sk;
   sk.partials = scr.partials;
-  sk.counters = scr.counters;
   sk.tiles_m = int((g.M + kGemmBM - 1) / kGemmBM);
   sk.tiles_n = int((g.N + kGemmBN - 1) / kGemmBN);
   sk.KT = g.K / kGemmBK;
@@ -181,6 +173,8 @@ void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s) {
   sk.split = p.split;
   const unsigned grid = unsigned(p.dp_units + p.tail * p.split);
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
+  if (p.tail > 0)
+    hipLaunchKernelGGL((gemm_bf16_tail_reduce_kernel<EPI>), dim3(unsigned(p.tail * 4)), dim3(128), 0, s, g, sk);
 }
 
 template <int EPI>
@@ -316,13 +310,6 @@ int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle) {
       (void)hipGetLastError();
       return fail(PBLOCK_ERR_NOMEM, std::string("hipMalloc workspace: ") + hipGetErrorString(e));
     }
-    // stream-K arrival counters start at zero; every launch leaves them at zero
-    e = hipMemset(static_cast<char*>(h->ws) + h->lay.counters, 0, size_t(h->lay.total - h->lay.counters));
-    if (e != hipSuccess) {
-      (void)hipFree(h->ws);
-      delete h;
-      return fail(PBLOCK_ERR_HIP, std::string("hipMemset counters: ") + hipGetErrorString(e));
-    }
     *out_handle = h;
     return PBLOCK_OK;
   } catch (...) {
@@ -433,7 +420,6 @@ int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pbl
     void* ag = base + h->lay.ag;
     SkScratch scr;
     scr.partials = reinterpret_cast<float*>(base + h->lay.partials);
-    scr.counters = reinterpret_cast<int*>(base + h->lay.counters);
     scr.G = h->n_cu;
 
     std::array<hipEvent_t, kTimedKernels + 1>* ev = nullptr;
