@@ -31,7 +31,9 @@ DEFAULT_WORKLOAD = "shard175b"
 # runs, scaled by the same counters read on a plain copy of known size.  Bytes
 # per launch; None until measured for the current kernel build.
 MEASURED_TRAFFIC_BYTES = {
-    "shard175b": None,
+    # gemm_in main kernel + its split-K tail reduce, 4-stage 32-wide-slab GEMM build
+    # (profiles/shard175b_kernels.md)
+    "shard175b": 1026821580,
 }
 
 WORKLOAD_NOTES = {
