@@ -39,6 +39,16 @@ struct AttnArgs {
 
 constexpr int kAttnBQ = 128;
 constexpr int kAttnBKV = 64;
+// Largest gap (log2 units) between a tile max and the reference max before rescaling.
+constexpr float kRescaleSlack = 8.0f;
+constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+// Value held by the lane 32 apart (lanes l and l^32 exchange through a half-wave swap).
+__device__ __forceinline__ float other_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  // lanes < 32: r[1] holds the upper half's value, r[0] its own; lanes >= 32 the reverse
+  return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+}
 
 template <int HD>
 __global__ __launch_bounds__(256, 2) void swa_attn_bf16_kernel(AttnArgs a) {
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn_bf16_kernel(AttnArgs a) {
   for (int t = 0; t < NH; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
-  float m_run = -INFINITY, l_part = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;  // m_run: reference max in log2 units
 
   load_kv(t_begin);
   store_kv(0);
@@ -151,47 +161,57 @@ __global__ __launch_bounds__(256, 2) void swa_attn_bf16_kernel(AttnArgs a) {
           sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[t2], 0, 0, 0);
         }
       }
-      // lane owns query my_q and keys j0 + t2*32 + 8*(r/4) + 4*lg + (r%4)
+      // lane owns query my_q and keys j0 + t2*32 + 8*(r/4) + 4*lg + (r%4); a key is in the
+      // band iff 0 <= my_q - j < W, one unsigned compare against the lane's offset
       const bool full = (j0 + BKV - 1 <= wq0) && (j0 >= wq0 + 31 - W + 1);
+      if (!full) {
+        const int diff = my_q - j0 - 4 * lg;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int koff = t2 * 32 + 8 * (r >> 2) + (r & 3);
+            sacc[t2][r] = (uint32_t(diff - koff) < uint32_t(W)) ? sacc[t2][r] : -INFINITY;
+          }
+      }
       float mloc = -INFINITY;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = sacc[t2][r] * a.scale_log2;
-          if (!full) {
-            const int j = j0 + t2 * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-            if (j > my_q || j < my_q - W + 1) s = -INFINITY;
-          }
-          sacc[t2][r] = s;
-          mloc = fmaxf(mloc, s);
-        }
-      const float m_tile = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float m_new = fmaxf(m_run, m_tile);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      m_run = m_new;
-      l_part *= alpha;
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t2][r]);
+      // the other 32 keys of this query sit in the lane 32 apart
+      const float m_tile = fmaxf(mloc, other_half(mloc)) * a.scale_log2;
+      // The running max (log2 units) only moves when a tile exceeds it by more than
+      // kRescaleSlack: until then the unnormalised weights stay below 2^kRescaleSlack and
+      // the accumulators need no rescaling.  The final division by the row sum makes the
+      // result independent of which reference max was used.
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
+        m_run = m_new;
+        l_part *= alpha;
 #pragma unroll
-      for (int ht = 0; ht < NH; ++ht)
+        for (int ht = 0; ht < NH; ++ht)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[ht][r] *= alpha;
-      // P in bf16, as the B operand of O^T = V^T P^T: fragment tt covers keys tt*16 .. tt*16+15
+          for (int r = 0; r < 16; ++r) oacc[ht][r] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      // P in bf16, as the B operand of O^T = V^T P^T: fragment tt covers keys tt*16 .. tt*16+15.
+      // The row sum adds the rounded weights, the same values the product uses.
       bf16x8 pf[4];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          uint32_t w[4];
+          bf16x2 w[4];
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = exp2f(sacc[t2][8 * hh + 2 * e2] - m_use);
-            const float p1 = exp2f(sacc[t2][8 * hh + 2 * e2 + 1] - m_use);
-            l_part += p0 + p1;
-            w[e2] = pack_bf16x2(p0, p1);
+            const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sacc[t2][8 * hh + 2 * e2], a.scale_log2, -m_use)),
+                              __builtin_amdgcn_exp2f(fmaf(sacc[t2][8 * hh + 2 * e2 + 1], a.scale_log2, -m_use))};
+            w[e2] = __builtin_convertvector(pp, bf16x2);
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(w[e2], kOnesBf16x2, l_part, false);
           }
-          const u32x4 u = {w[0], w[1], w[2], w[3]};
-          pf[t2 * 2 + hh] = __builtin_bit_cast(bf16x8, u);
+          pf[t2 * 2 + hh] = bf16x8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
         }
 #pragma unroll
       for (int ht = 0; ht < NH; ++ht) {
@@ -209,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn_bf16_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  const float l = l_part + __shfl_xor(l_part, 32, 64);
+  const float l = l_part + other_half(l_part);
   if (my_q < S) {
     const float inv = 1.0f / l;
     uint16_t* orow = a.o + (int64_t(b) * S + my_q) * a.ld_o + h * HD;
