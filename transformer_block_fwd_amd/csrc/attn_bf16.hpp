@@ -140,6 +140,10 @@ __global__ __launch_bounds__(256, 2) void swa_attn_bf16_kernel(AttnArgs a) {
 
   load_kv(t_begin);
   store_kv(0);
+  // Every load issued so far (Q fragments included) must be complete here: otherwise the
+  // compiler carries the Q loads into the loop as pending and makes the first products of
+  // every tile wait for that tile's prefetch as well.
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   __syncthreads();
 
   for (int t = t_begin; t <= t_end; ++t) {
