@@ -90,9 +90,11 @@ typedef struct pblock_s* pblock_t;
 int pblock_validate_cfg(const pblock_cfg* cfg);
 
 /* Bytes of device workspace a handle for cfg allocates, or a negative status.
- * Host only.  The workspace holds the intermediates u, QKV, AG and, for bf16,
- * the GEMM scratch for the split-K tail wave: one fp32 256x256 partial tile
- * per compute unit (this estimate assumes 256). */
+ * Host only.  The workspace holds the intermediates u [Mt, d], QKV [M, 3*H*hd],
+ * AG [Mt, H*hd + ffn] (M = B*S; the GEMM row operands u and AG are allocated
+ * in whole 256-row tiles, Mt = M rounded up to 256) and, for bf16, the GEMM
+ * scratch for the split-K tail wave: one fp32 256x256 partial tile per
+ * compute unit (this estimate assumes 256). */
 int64_t pblock_workspace_bytes(const pblock_cfg* cfg);
 
 /* Algorithmic FLOPs of one forward for cfg: 2*M*d*(3*H*hd+ffn) +

@@ -74,7 +74,8 @@ def test_workspace_and_flops():
     for cfg in CONFIGS.values():
         es = 2 if cfg.dtype == "bf16" else 4
         ws = tb.pblock_workspace_bytes(cfg)
-        need = es * cfg.M * (cfg.d + 3 * cfg.A + cfg.k_out)
+        mt = -(-cfg.M // 256) * 256  # GEMM row operands u, AG come in whole 256-row tiles
+        need = es * (mt * cfg.d + cfg.M * 3 * cfg.A + mt * cfg.k_out)
         slack = 5 * 256
         if cfg.dtype == "bf16":
             # GEMM scratch (host estimate at 256 CUs): one fp32 256x256 partial tile per CU

@@ -4,21 +4,31 @@
 // weights [N, K]), which is what the 32x32x16 bf16 MFMA wants: every lane
 // feeds 8 consecutive k of one row from a single 16-byte LDS read.
 //
-// Tile: 256 x 256 outputs per workgroup of 8 wavefronts (2 per SIMD), laid
-// out 2 (M) x 4 (N); each wavefront owns 128 x 64 as 4 x 2 MFMA tiles of
-// 32 x 32 with fp32 accumulators.
+// Tile: 256 x 256 outputs per workgroup of 4 wavefronts (one per SIMD), laid
+// out 2 (M) x 2 (N); each wavefront owns 128 x 128 as 4 x 4 MFMA tiles of
+// 32 x 32 whose fp32 accumulators (256 per lane) live in the AGPR file.
 //
-// Pipeline: the k loop walks 32-wide slabs through four LDS stages (4 x 32 KiB,
-// each a separately named array so the compiler can see that filling one
-// stage never aliases reading another).  Global data moves straight into LDS
-// with global_load_lds_dwordx4 (no staging registers), three slabs ahead of
-// the MFMAs; each step waits only until this wave's copies of the current
-// slab have landed (s_waitcnt vmcnt with the two later slabs still in flight),
-// then one barrier publishes the slab and frees the stage read one step
-// earlier for the next prefetch.  Each copy instruction fills 1 KiB = 16 rows
-// of 64 bytes; the 16-byte chunk index inside a row is XORed with
-// ((row >> 1) & 3) on the source side and undone on the fragment reads.
-// Rows past M or N are clamped to the last valid row (never stored).
+// Pipeline: the k loop walks 64-wide slabs through two LDS stages (each an A
+// and a B array of 32 KiB, separately named so the compiler can see that
+// filling one never aliases reading another).  Global data moves straight
+// into LDS with global_load_lds_dwordx4; one instruction fills 1 KiB = 8 rows
+// of 128 bytes, the 16-byte chunk index inside a row XORed with
+// ((row >> 1) & 7) on the source side and undone on the fragment reads (the 16
+// rows one read pass touches then hit 16 distinct bank groups).  Within a
+// slab (four 16-deep k-steps of 16 MFMAs per wavefront):
+//   k-step 0: its MFMAs run while the fragments of k-steps 1..3 are read, so
+//     the whole stage is consumed early; a barrier then frees it;
+//   k-steps 1..3: the copies of slab t+2 into the freed stage are spread over
+//     these MFMAs (6 + 4 + 6 instructions per wavefront), so the load unit sees
+//     an even stream instead of a burst;
+//   before k-step 3: wait for this wave's copies of slab t+1, barrier, and
+//     read k-step 0 of slab t+1 behind the k-step 3 MFMAs.
+// The MFMA / LDS-read / copy interleave is pinned with sched_group_barrier.
+//
+// Operand bounds: A rows are read up to the end of the last 256-row tile (the
+// caller allocates A in whole 256-row tiles; rows past M are never stored); B
+// has N % 8 == 0 rows and an 8-row block past N is clamped as a whole to the
+// last block.  K % 64 == 0.
 //
 // Schedule: data-parallel waves plus a split-K tail.  With G workgroups
 // resident at once (one per CU), the first floor(T / G) * G tiles run whole,
@@ -35,12 +45,15 @@
 // block of tiles at the same k, so they share activation and weight slabs in
 // that XCD's L2.
 //
-// Epilogues:
+// Epilogue: the accumulators go out through LDS in four rounds of 64 rows
+// (fp32, chunk-permuted), so every global store is a full 16-byte piece of a
+// row and a wavefront writes whole 512-byte rows.
 //   kEpiSplitGelu: columns < nsplit are stored as bf16 to out0 (the Q|K|V
 //     projections); columns >= nsplit get the exact GeLU and go to out1 at
 //     column off1 + (n - nsplit) (the FC1 activations next to the attention
 //     output, so the second GEMM reads one K-contiguous operand).
 //   kEpiResidual: optional residual x added in fp32, one rounding to bf16.
+// nsplit, the strides and off1 are multiples of 8.
 #pragma once
 
 #include "common.hpp"
@@ -63,12 +76,12 @@ struct GemmArgs {
   int64_t ldr;
 };
 
-constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 32, kGemmThreads = 512, kGemmStages = 4;
-constexpr int kGemmStage = (kGemmBM + kGemmBN) * kGemmBK;  // elements per LDS stage (32 KiB)
+constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 64, kGemmThreads = 256;
+constexpr int kGemmHalf = 256 * kGemmBK;  // elements of one operand tile of a stage (32 KiB)
 
 // Work decomposition of one GEMM launch (grid = dp_units + tail * split).
 struct GemmSched {
-  float* partials;  // [tail * split][kGemmBM * kGemmBN] fp32 (chunk slot, then float4 row, then thread)
+  float* partials;  // [tail * split][kGemmBM * kGemmBN] fp32 (chunk slot, then float4 index, then thread)
   int tiles_m, tiles_n;
   int KT;           // k slabs per tile
   int dp_units;     // tiles computed whole (a multiple of the resident workgroup count)
@@ -102,9 +115,11 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier that no memory access may be moved across (the waits are explicit).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Epilogue of 4 consecutive columns n .. n+3 of row m (tail-reduce path).
 template <int EPI>
 __device__ __forceinline__ void store_outputs(const GemmArgs& g, int m, int n, float v0, float v1, float v2, float v3) {
   uint16_t* dst;
@@ -129,27 +144,48 @@ __device__ __forceinline__ void store_outputs(const GemmArgs& g, int m, int n, f
   *reinterpret_cast<u32x2*>(dst) = o;
 }
 
+// Epilogue of 8 consecutive columns n .. n+7 of row m, one 16-byte store.
+template <int EPI>
+__device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f32x4 lo, f32x4 hi) {
+  float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  uint16_t* dst;
+  if constexpr (EPI == kEpiSplitGelu) {
+    if (n < g.nsplit) {
+      dst = g.out0 + int64_t(m) * g.ld0 + n;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+      dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
+    }
+  } else {
+    if (g.resid != nullptr) {
+      const u32x4 xr = *reinterpret_cast<const u32x4*>(g.resid + int64_t(m) * g.ldr + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] += __uint_as_float(xr[e] << 16);
+        v[2 * e + 1] += __uint_as_float(xr[e] & 0xFFFF0000u);
+      }
+    }
+    dst = g.out0 + int64_t(m) * g.ld0 + n;
+  }
+  const u32x4 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  *reinterpret_cast<u32x4*>(dst) = o;
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, GemmSched sk) {
-  constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, NT = kGemmThreads, NSTAGE = kGemmStages;
-  constexpr int STAGE = kGemmStage;
-  constexpr int WN = 4, TM = 128, TN = 64, FM = 4, FN = 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st3[STAGE];
-  auto stage_ptr = [&](int s) -> uint16_t* { return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3; };
+  constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, NT = kGemmThreads;
+  constexpr int FM = 4, FN = 4;  // 32x32 MFMA tiles per wavefront (128 x 128)
+  __shared__ __attribute__((aligned(1024))) uint16_t a0[kGemmHalf];
+  __shared__ __attribute__((aligned(1024))) uint16_t b0[kGemmHalf];
+  __shared__ __attribute__((aligned(1024))) uint16_t a1[kGemmHalf];
+  __shared__ __attribute__((aligned(1024))) uint16_t b1[kGemmHalf];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lg = lane >> 5;
-  // DMA: lane l of a 1 KiB block fills row l/4 (of 16), physical chunk l%4 = logical chunk ^ ((row>>1)&3)
-  const int dma_row = lane >> 2;
-  const int dma_chunk = (lane & 3) ^ ((lane >> 3) & 3);
-  const int a_row0 = wm * TM + lr;
-  const int b_row0 = wn * TN + lr;
-  const int swz = (lr >> 1) & 3;
 
   int L, kb, ke, tl = -1, chunk = 0;
   if (int(blockIdx.x) < sk.dp_units) {
@@ -169,26 +205,40 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   tile_coords(L, sk.tiles_m, sk.tiles_n, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const uint16_t* a_src[2];
-  const uint16_t* b_src[2];
+  // Copies: instruction i (0..7) of wave w fills 1 KiB block 8w + i of each operand tile =
+  // rows 64w + 8i + l/8; lane l writes physical chunk l%8, fetched from logical chunk
+  // (l%8) ^ ((row >> 1) & 7) = (l%8) ^ (4*(i&1) + l/16).
+  const uint32_t lda_b = uint32_t(g.lda) * 2u, ldb_b = uint32_t(g.ldb) * 2u;
+  uint32_t offa[2], offb[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ra = min(m0 + wave * 32 + 16 * i + dma_row, g.M - 1);
-    const int rb = min(n0 + wave * 32 + 16 * i + dma_row, g.N - 1);
-    a_src[i] = g.a + int64_t(ra) * g.lda + dma_chunk * 8;
-    b_src[i] = g.b + int64_t(rb) * g.ldb + dma_chunk * 8;
+  for (int p = 0; p < 2; ++p) {
+    const int lc = (lane & 7) ^ (4 * p + (lane >> 4));
+    offa[p] = uint32_t(lane >> 3) * lda_b + uint32_t(lc << 4);
+    offb[p] = uint32_t(lane >> 3) * ldb_b + uint32_t(lc << 4);
   }
-  auto issue = [&](int kt, uint16_t* stage) {
-    const int koff = kt * BK;
-    uint16_t* sa = stage + wave * 2 * 512;
-    uint16_t* sb = stage + BM * BK + wave * 2 * 512;
+  const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(g.a) + int64_t(m0 + wave * 64) * lda_b;
+  // copy instructions i0 .. i1-1 (one A and one B instruction each) of slab kt
+  auto issue = [&](int kt, uint16_t* sa, uint16_t* sb, int i0, int i1) __attribute__((always_inline)) {
+    const uint32_t kofs = uint32_t(kt) * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(a_src[i] + koff, (PBLK_LDS void*)(sa + i * 512), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(b_src[i] + koff, (PBLK_LDS void*)(sb + i * 512), 16, 0, 0);
+    for (int i = i0; i < i1; ++i) {
+      __builtin_amdgcn_global_load_lds(a_blk + int64_t(8 * i) * lda_b + kofs + offa[i & 1],
+                                       (PBLK_LDS void*)(sa + (wave * 8 + i) * 512), 16, 0, 0);
+      const int brow = min(n0 + wave * 64 + 8 * i, g.N - 8);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(g.b) + int64_t(brow) * ldb_b + kofs + offb[i & 1],
+                                       (PBLK_LDS void*)(sb + (wave * 8 + i) * 512), 16, 0, 0);
+    }
   };
+
+  // Fragment reads: row w*128 + i*32 + lr, logical chunk 2kk + lg at physical chunk
+  // (2kk + lg) ^ ((lr >> 1) & 7); byte offsets within an operand tile.
+  uint32_t rda[4], rdb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint32_t o = uint32_t(lr * 128 + (((2 * kk + lg) ^ ((lr >> 1) & 7)) << 4));
+    rda[kk] = o + uint32_t(wm * 128 * 128);
+    rdb[kk] = o + uint32_t(wn * 128 * 128);
+  }
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -198,54 +248,88 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](const uint16_t* stage) {
-    const uint16_t* sa = stage;
-    const uint16_t* sb = stage + BM * BK;
+  bf16x8 fa[4][FM], fb[4][FN];  // one fragment buffer per k-step of a slab
+  auto rd = [&](int buf, const uint16_t* sa, const uint16_t* sb, int kk) __attribute__((always_inline)) {
+    const uint8_t* pa = reinterpret_cast<const uint8_t*>(sa);
+    const uint8_t* pb = reinterpret_cast<const uint8_t*>(sb);
+    // in the order the MFMAs consume them
+    fa[buf][0] = *reinterpret_cast<const bf16x8*>(pa + rda[kk]);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = ((kk * 2 + lg) ^ swz) << 3;
-      bf16x8 af[FM], bfr[FN];
+    for (int j = 0; j < FN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8*>(pb + rdb[kk] + j * 32 * 128);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + (a_row0 + i * 32) * BK + ch);
+    for (int i = 1; i < FM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8*>(pa + rda[kk] + i * 32 * 128);
+  };
+  auto mm = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (b_row0 + j * 32) * BK + ch);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  };
+  // sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read
+  // 16 MFMAs with 24 fragment reads behind the first 12
+  auto interleave_rd24 = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int x = 0; x < 12; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  // 16 MFMAs with n copy instructions and nr fragment reads spread over them
+  auto interleave_cp = [&](int n, int nr) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    for (int x = 0; x < 16; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (x < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (x < n) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   };
 
-  // prologue: slabs kb .. kb+NSTAGE-2 into stages 0 .. NSTAGE-2, issued unconditionally
-  // (a segment shorter than that reloads its last slab) so the wait counts below are exact
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) issue(min(kb + s, ke - 1), stage_ptr(s));
+  // Slab t in stage (ca, cb), its k-step 0 fragments requested into buffer 0, the copies of
+  // slab t+1 into stage (na, nb) in flight.
+  auto slab = [&](int t, const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb) __attribute__((always_inline)) {
+    uint16_t* wa = const_cast<uint16_t*>(ca);
+    uint16_t* wb = const_cast<uint16_t*>(cb);
+    const int tc = min(t + 2, ke - 1);  // branch-free: past the end the last slab is fetched again
+    rd(1, ca, cb, 1);
+    rd(2, ca, cb, 2);
+    rd(3, ca, cb, 3);
+    mm(0);
+    interleave_rd24();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();   // own reads of this stage done
+    lds_barrier();  // everyone's: the stage is free
+    issue(tc, wa, wb, 0, 3);
+    mm(1);
+    interleave_cp(6, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(tc, wa, wb, 3, 5);
+    mm(2);
+    interleave_cp(4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_lgkm0<10>();  // own copies of slab t+1 landed (10 of slab t+2 may be in flight)
+    lds_barrier();        // everyone's: slab t+1 is complete
+    issue(tc, wa, wb, 5, 8);
+    rd(0, na, nb, 0);
+    mm(3);
+    interleave_cp(6, 8);
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // steady state: every step has NSTAGE-2 later slabs in flight and prefetches one more
+  issue(kb, a0, b0, 0, 8);
+  issue(min(kb + 1, ke - 1), a1, b1, 0, 8);
+  wait_vm_lgkm0<16>();  // slab kb landed
+  lds_barrier();
+  rd(0, a0, b0, 0);
+  const int n = ke - kb;
   int kt = kb;
-  for (; kt + 2 * NSTAGE - 1 <= ke; kt += NSTAGE) {
-#pragma unroll
-    for (int q = 0; q < NSTAGE; ++q) {
-      wait_vm_lgkm0<4 * (NSTAGE - 2)>();
-      lds_barrier();
-      issue(kt + q + NSTAGE - 1, stage_ptr((q + NSTAGE - 1) % NSTAGE));
-      compute(stage_ptr(q));
-    }
+  for (int p = 0; p + 2 <= n; p += 2, kt += 2) {
+    slab(kt, a0, b0, a1, b1);
+    slab(kt + 1, a1, b1, a0, b0);
   }
-  // the last (fewer than 2*NSTAGE-1) slabs: drain with full waits
-#pragma unroll
-  for (int q = 0; q < 2 * NSTAGE - 1; ++q) {
-    const int j = kt + q;
-    if (j < ke) {
-      wait_vm_lgkm0<0>();
-      lds_barrier();
-      if (j + NSTAGE - 1 < ke) issue(j + NSTAGE - 1, stage_ptr((q + NSTAGE - 1) % NSTAGE));
-      compute(stage_ptr(q % NSTAGE));
-    }
-  }
+  if (n & 1) slab(kt, a0, b0, a1, b1);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no copy may still be writing this workgroup's LDS
 
   if (tl >= 0) {
     constexpr int TILE4 = BM * BN / 4;
@@ -262,33 +346,50 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
         }
     return;
   }
+
+  // Epilogue through LDS, four rounds: in round i every wave stages its rows wm*128 + i*32 +
+  // 0..31 as fp32 (stage pair i&1, the wm half in its own array, 16-byte chunks XOR-permuted
+  // by row), then all threads store 64 full rows with 16-byte writes.  Lane (lr, lg) of MFMA
+  // tile (i, j) holds row lr and columns j*32 + 8*(r/4) + 4*lg + r%4.
+  lds_barrier();  // every wave is past its last fragment read
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * TM + i * 32 + lr;
-    if (m >= g.M) continue;
+    float* mine = reinterpret_cast<float*>((i & 1) ? (wm ? b1 : a1) : (wm ? b0 : a0));
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = n0 + wn * TN + j * 32 + r4 * 8 + lg * 4;
-        if (n >= g.N) continue;
-        store_outputs<EPI>(g, m, n, acc[i][j][r4 * 4], acc[i][j][r4 * 4 + 1], acc[i][j][r4 * 4 + 2],
-                           acc[i][j][r4 * 4 + 3]);
+        const int c = wn * 32 + j * 8 + r4 * 2 + lg;
+        const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+        *reinterpret_cast<f32x4*>(mine + lr * 256 + ((c ^ (lr & 15)) << 2)) = v;
       }
+    lds_barrier();
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int r = p * 8 + (tid >> 5);
+      const int half = r >> 5, lrow = r & 31;
+      const float* src = reinterpret_cast<const float*>((i & 1) ? (half ? b1 : a1) : (half ? b0 : a0));
+      const int c0 = (tid & 31) * 2;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src + lrow * 256 + ((c0 ^ (lrow & 15)) << 2));
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + lrow * 256 + (((c0 + 1) ^ (lrow & 15)) << 2));
+      const int m = m0 + half * 128 + i * 32 + lrow;
+      const int nn = n0 + (tid & 31) * 8;
+      if (m < g.M && nn < g.N) store_chunk8<EPI>(g, m, nn, lo, hi);
+    }
   }
 }
 
 // Sums the k-chunk partials of each tail tile in chunk order and applies the epilogue.
-// grid = tail * 4 workgroups of 128 threads; workgroup (tile, quarter) handles the
-// main kernel's threads [128*quarter, 128*quarter + 128) of that tile.
+// grid = tail * 2 workgroups of 128 threads; workgroup (tile, half) handles the main
+// kernel's threads [128*half, 128*half + 128) of that tile.
 template <int EPI>
 __global__ __launch_bounds__(128) void gemm_bf16_tail_reduce_kernel(GemmArgs g, GemmSched sk) {
   constexpr int BM = kGemmBM, BN = kGemmBN, NT = kGemmThreads;
-  constexpr int WN = 4, TM = 128, TN = 64, FM = 4, FN = 2;
-  const int tl = blockIdx.x >> 2;
-  const int tid = (blockIdx.x & 3) * 128 + threadIdx.x;
+  constexpr int FM = 4, FN = 4;
+  const int tl = blockIdx.x >> 1;
+  const int tid = (blockIdx.x & 1) * 128 + threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lg = lane >> 5;
   int tm, tn;
   tile_coords(sk.dp_units + tl, sk.tiles_m, sk.tiles_n, &tm, &tn);
@@ -297,7 +398,7 @@ __global__ __launch_bounds__(128) void gemm_bf16_tail_reduce_kernel(GemmArgs g, 
   const f32x4* base = reinterpret_cast<const f32x4*>(sk.partials) + int64_t(tl * sk.split) * TILE4;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * TM + i * 32 + lr;
+    const int m = m0 + wm * 128 + i * 32 + lr;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -305,7 +406,7 @@ __global__ __launch_bounds__(128) void gemm_bf16_tail_reduce_kernel(GemmArgs g, 
         const int r4 = (i * FN + j) * 4 + q;
         f32x4 s = base[r4 * NT + tid];
         for (int c = 1; c < sk.split; ++c) s += base[int64_t(c) * TILE4 + r4 * NT + tid];
-        const int n = n0 + wn * TN + j * 32 + q * 8 + lg * 4;
+        const int n = n0 + wn * 128 + j * 32 + q * 8 + lg * 4;
         if (m < g.M && n < g.N) store_outputs<EPI>(g, m, n, s[0], s[1], s[2], s[3]);
       }
   }

@@ -78,11 +78,14 @@ WsLayout ws_layout(const pblock_cfg* c, int G) {
   const Dims dm = dims(c);
   const int es = elem_size(c->dtype);
   if (G <= 0) G = 256;
+  // u and ag are the GEMMs' row operands: allocated in whole 256-row tiles, since the bf16
+  // GEMM reads its A operand up to the end of the last tile (rows past M are never stored)
+  const int64_t m_tiles = (dm.M + kGemmBM - 1) / kGemmBM * kGemmBM;
   WsLayout w;
   w.u = 0;
-  w.qkv = align256(dm.M * c->d * es);
+  w.qkv = align256(m_tiles * c->d * es);
   w.ag = w.qkv + align256(dm.M * 3 * dm.A * es);
-  w.partials = w.ag + align256(dm.M * dm.k_out * es);
+  w.partials = w.ag + align256(m_tiles * dm.k_out * es);
   int64_t part_bytes = 0;
   if (c->dtype == PBLOCK_BF16) {
     // the split-K tail holds at most G chunks (one wave)
@@ -174,7 +177,7 @@ void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s) {
   const unsigned grid = unsigned(p.dp_units + p.tail * p.split);
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
   if (p.tail > 0)
-    hipLaunchKernelGGL((gemm_bf16_tail_reduce_kernel<EPI>), dim3(unsigned(p.tail * 4)), dim3(128), 0, s, g, sk);
+    hipLaunchKernelGGL((gemm_bf16_tail_reduce_kernel<EPI>), dim3(unsigned(p.tail * 2)), dim3(128), 0, s, g, sk);
 }
 
 template <int EPI>
