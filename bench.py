@@ -32,7 +32,8 @@ DEFAULT_WORKLOAD = "shard175b"
 # per launch; None until measured for the current kernel build.
 MEASURED_TRAFFIC_BYTES = {
     # gemm_in main kernel + its split-K tail reduce (profiles/shard175b_kernels.md); set
-    # only for the GEMM build the counters were taken on
+    # only for the GEMM build the counters were taken on (4-wave 128x128, 64-deep slabs)
+    "shard175b": 1025501926,
 }
 
 WORKLOAD_NOTES = {
