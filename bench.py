@@ -8,11 +8,14 @@ local heads x 128, local ffn 6144, W=512), emitting the pre-reduce-scatter
 partial.
 
 Prints ONE JSON line: throughput in TFLOP/s of algorithmic work, % of the bf16
-MFMA peak, tokens/s, per-kernel times measured with HIP events inside the
-timed region, the roofline record of the dominant kernel, and the fp64 CPU
-oracle timed on the host as a baseline.
+MFMA peak, tokens/s, step-time median / p10 / p90, a cold-cache pass, per-kernel
+times measured with HIP events inside the timed region, the roofline record of
+the dominant kernel, the rate of a register-only MFMA loop measured in the same
+run, and the fp64 CPU oracle timed on the host as a baseline.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload shard175b]
+                  [--block parallel|serial] [--window W]
+  python bench.py --sweep      # attention time against window and sequence length
 """
 from __future__ import annotations
 
@@ -26,6 +29,7 @@ METRIC = "parallel-block fwd TFLOP/s and % of bf16 MFMA peak; tokens/s (1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
 DEFAULT_WORKLOAD = "shard175b"
+COLD_SCRUB_MIB = 512       # written between cold-cache steps (more than the 256 MB last-level cache)
 
 # HBM traffic of the dominant kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs, scaled by the same counters read on a plain copy of known size.  Bytes
@@ -50,9 +54,17 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--block", choices=("parallel", "serial"), default="parallel",
+                   help="the parallel block (default) or the serial pre-LN layer from the same kernels")
+    p.add_argument("--window", type=int, default=0, help="override the workload's attention window W")
+    p.add_argument("--add-residual", type=int, choices=(0, 1), default=None,
+                   help="override the workload's add_residual (the serial form always adds it)")
+    p.add_argument("--cold-steps", type=int, default=10, help="cold-cache steps after the timed run (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (for HBM counter calibration) and exit")
+    p.add_argument("--sweep", action="store_true",
+                   help="only time the attention kernel over windows and sequence lengths and fit time vs keys")
     return p.parse_args()
 
 
@@ -68,7 +80,7 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
 
 
-def cpu_baseline(cfg, inp) -> dict:
+def cpu_baseline(cfg, inp, block, ln2) -> dict:
     """The fp64 oracle, as it stands, timed once on the host cores over the whole workload."""
     import oracle
 
@@ -79,12 +91,95 @@ def cpu_baseline(cfg, inp) -> dict:
     except Exception:  # noqa: BLE001
         threads = os.cpu_count() or 1
     t0 = time.perf_counter()
-    oracle.block_forward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W, eps=cfg.ln_eps,
-                         add_residual=bool(cfg.add_residual))
+    if block == "serial":
+        oracle.serial_block_forward(inp.x, inp.gamma, inp.beta, ln2["gamma2"], ln2["beta2"], inp.w_in, inp.w_out,
+                                    cfg.H, cfg.hd, cfg.W, eps=cfg.ln_eps)
+    else:
+        oracle.block_forward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W, eps=cfg.ln_eps,
+                             add_residual=bool(cfg.add_residual))
     dt = time.perf_counter() - t0
     return {"value": round(cfg.flops() / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 3), "tokens_per_s": round(cfg.M / dt, 1),
             "sample": f"one full forward of the {cfg.name} workload (all {cfg.M} tokens), float64 numpy"}
+
+
+def percentile(v, q):
+    s = sorted(v)
+    k = (len(s) - 1) * q
+    lo, hi = int(k), min(int(k) + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (k - lo)
+
+
+def mfma_loop_rate(tb, torch, stream) -> float:
+    """TFLOP/s of the library's register-only MFMA loop over all CUs (about 20 ms)."""
+    wgs = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    iters = 4000
+    tb.pblock_mfma_loop(wgs, 100, sink, stream)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    tb.pblock_mfma_loop(wgs, iters, sink, stream)
+    e.record(stream)
+    torch.cuda.synchronize()
+    return wgs * 4 * iters * 16 * 32768 / (s.elapsed_time(e) * 1e-3) / 1e12
+
+
+def attention_sweep() -> None:
+    """Attention kernel time against the number of (query, key) pairs it must score:
+    W in {128 .. 2048} at S = 8192 and S in {2048, 4096} at W = 1024 (the long
+    workload's heads), a least-squares line through the points, and the full-causal
+    workload's attention against that line's prediction."""
+    import numpy as np
+    import torch
+
+    import transformer_block_fwd_amd as tb
+    from workload import CONFIGS
+
+    base = CONFIGS["long"]
+    H, hd = base.H, base.hd
+    A = H * hd
+    torch.manual_seed(0)
+    stream = torch.cuda.current_stream()
+
+    def time_attention(B, S, W, reps=20):
+        qkv = torch.randn(B * S, 3 * A, device="cuda", dtype=torch.bfloat16)
+        o = torch.empty(B * S, A, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            tb.pblock_swa_attention(qkv, 3 * A, o, A, B, S, H, hd, W, "bf16", stream)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            tb.pblock_swa_attention(qkv, 3 * A, o, A, B, S, H, hd, W, "bf16", stream)
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    def pairs(B, S, W):
+        w = min(W, S)
+        return B * H * (S * w - w * (w - 1) // 2)
+
+    points = []
+    for S, W in [(8192, w) for w in (128, 256, 512, 1024, 2048)] + [(2048, 1024), (4096, 1024)]:
+        ms = time_attention(1, S, W)
+        points.append({"B": 1, "S": S, "W": W, "pairs": pairs(1, S, W), "ms": round(ms, 5),
+                       "tflops": round(4 * hd * pairs(1, S, W) / (ms * 1e-3) / 1e12, 1)})
+        print(f"[sweep] S={S} W={W}: {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    x = np.array([p["pairs"] for p in points], dtype=np.float64)
+    y = np.array([p["ms"] for p in points], dtype=np.float64)
+    slope, icpt = np.polyfit(x, y, 1)
+    r2 = 1.0 - float(((y - (slope * x + icpt)) ** 2).sum() / ((y - y.mean()) ** 2).sum())
+    fc = CONFIGS["fullcausal"]
+    ms_fc = time_attention(fc.B, fc.S, fc.W)
+    pred_fc = slope * pairs(fc.B, fc.S, fc.W) + icpt
+    print(json.dumps({
+        "sweep": "swa_attention bf16, 32 heads x 128 (the long workload's heads)",
+        "points": points,
+        "fit": {"ms_per_gpair": round(slope * 1e9, 6), "intercept_ms": round(icpt, 5), "r2": round(r2, 5)},
+        "fullcausal_check": {"B": fc.B, "S": fc.S, "W": fc.W, "ms": round(ms_fc, 5), "predicted_ms": round(pred_fc, 5),
+                             "ratio": round(ms_fc / pred_fc, 3)},
+    }), flush=True)
 
 
 def main():
@@ -99,16 +194,27 @@ def main():
     import torch
 
     import transformer_block_fwd_amd as tb
-    from workload import CONFIGS, make_inputs
+    from workload import CONFIGS, make_inputs, make_ln2
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.sweep:
+        attention_sweep()
+        return
 
     cfg = CONFIGS[args.workload]
-    print(f"[bench] workload {cfg}", file=sys.stderr, flush=True)
+    if args.window:
+        cfg = cfg.replace(W=args.window)
+    if args.add_residual is not None:
+        cfg = cfg.replace(add_residual=args.add_residual)
+    if args.block == "serial":
+        cfg = cfg.replace(add_residual=1)  # the serial form's residual stream
+    print(f"[bench] workload {cfg} block {args.block}", file=sys.stderr, flush=True)
     inp = make_inputs(cfg, seed=0)
     arrs = inp.device_arrays()
+    ln2 = make_ln2(cfg, seed=0)
+    arrs["gamma2"], arrs["beta2"] = ln2["gamma2_dev"], ln2["beta2_dev"]
     if cfg.dtype == "bf16":
         dev = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).cuda()
                for k, v in arrs.items()}
@@ -119,39 +225,69 @@ def main():
     stream = torch.cuda.current_stream()
     h = tb.pblock_create(cfg)
 
+    def step():
+        if args.block == "serial":
+            tb.pblock_forward_serial(h, dev["x"], weights, (dev["gamma2"], dev["beta2"]), cfg, out, stream)
+        else:
+            tb.pblock_forward(h, dev["x"], weights, cfg, out, stream)
+
     for _ in range(args.warmup):
-        tb.pblock_forward(h, dev["x"], weights, cfg, out, stream)
+        step()
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
 
     tb.pblock_set_timing(h, True)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        tb.pblock_forward(h, dev["x"], weights, cfg, out, stream)
-    end.record(stream)
+    marks[0].record(stream)
+    for i in range(args.steps):
+        step()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(end)
+    ms_total = marks[0].elapsed_time(marks[-1])
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     kernel_ms, n_fwd = tb.pblock_kernel_times(h)
     tb.pblock_set_timing(h, False)
     print(f"[bench] timed {args.steps} steps in {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms)", file=sys.stderr,
           flush=True)
+
+    cold = None
+    if args.cold_steps > 0:
+        scrub = torch.empty(COLD_SCRUB_MIB << 20, dtype=torch.uint8, device="cuda")
+        cold_ms = []
+        for i in range(args.cold_steps):
+            scrub.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(e0.elapsed_time(e1))
+        del scrub
+        med = percentile(cold_ms, 0.5)
+        cold = {"steps": args.cold_steps, "scrub_mib": COLD_SCRUB_MIB, "median_ms": round(med, 5),
+                "tflops": round(cfg.flops() / (med * 1e-3) / 1e12, 3)}
+        print(f"[bench] cold-cache median {med:.3f} ms", file=sys.stderr, flush=True)
+
+    mfma_tflops = mfma_loop_rate(tb, torch, stream)
+    print(f"[bench] register-only MFMA loop {mfma_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     ms_step = ms_total / args.steps
     flops = cfg.flops()
     tflops = flops / (ms_step * 1e-3) / 1e12
     k_avg = {k: v / max(n_fwd, 1) for k, v in kernel_ms.items()}
     g1_ms = k_avg["gemm_in"]
-    g1_tflops = cfg.gemm1_flops() / (g1_ms * 1e-3) / 1e12
-    traffic = MEASURED_TRAFFIC_BYTES.get(cfg.name)
+    g1_flops = cfg.gemm1_flops()
+    as_profiled = args.block == "parallel" and not args.window and args.add_residual is None
+    traffic = MEASURED_TRAFFIC_BYTES.get(cfg.name) if as_profiled else None
     roofline = {"kernel": "gemm_in (fused QKV+FC1 GEMM, GeLU epilogue)", "bound": "mfma",
-                "achieved": round(g1_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g1_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "algorithmic_flops_per_launch": cfg.gemm1_flops(), "avg_launch_ms": round(g1_ms, 5)}
+                "achieved": round(g1_flops / (g1_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g1_flops / (g1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_flops_per_launch": g1_flops, "avg_launch_ms": round(g1_ms, 5)}
+    if args.block == "serial":
+        roofline["kernel"] = "gemm_in (QKV GEMM + FC1 GEMM with GeLU epilogue, summed per forward)"
     per_kernel = {}
     for k, ms in k_avg.items():
         kf = {"gemm_in": cfg.gemm1_flops(), "gemm_out": cfg.gemm2_flops(), "attention": cfg.attn_flops()}.get(k)
@@ -160,7 +296,8 @@ def main():
             rec["tflops"] = round(kf / (ms * 1e-3) / 1e12, 2)
         if k == "layernorm":
             es = 2 if cfg.dtype == "bf16" else 4
-            rec["gbs"] = round((2 * cfg.M * cfg.d * es + 2 * cfg.d * es) / (ms * 1e-3) / 1e9, 1)
+            n_ln = 2 if args.block == "serial" else 1
+            rec["gbs"] = round(n_ln * (2 * cfg.M * cfg.d * es + 2 * cfg.d * es) / (ms * 1e-3) / 1e9, 1)
         per_kernel[k] = rec
 
     result = {
@@ -176,12 +313,17 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
-        "config": {"workload": f"{cfg.name}: {WORKLOAD_NOTES.get(cfg.name, '')}", "B": cfg.B, "S": cfg.S,
-                   "d": cfg.d, "H": cfg.H, "hd": cfg.hd, "ffn": cfg.ffn, "W": cfg.W,
+        "config": {"workload": f"{cfg.name}: {WORKLOAD_NOTES.get(cfg.name, '')}", "block": args.block, "B": cfg.B,
+                   "S": cfg.S, "d": cfg.d, "H": cfg.H, "hd": cfg.hd, "ffn": cfg.ffn, "W": cfg.W,
                    "add_residual": cfg.add_residual, "parallelism": "single GPU"},
         "pct_peak_bf16": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.M / (ms_step * 1e-3), 1),
         "algorithmic_gflop_per_step": round(flops / 1e9, 3),
+        "step_ms": {"median": round(percentile(step_ms, 0.5), 5), "p10": round(percentile(step_ms, 0.1), 5),
+                    "p90": round(percentile(step_ms, 0.9), 5)},
+        "cold_cache": cold,
+        "mfma_loop_tflops": round(mfma_tflops, 1),
+        "pct_of_mfma_loop": round(100 * tflops / mfma_tflops, 2),
         "kernels": per_kernel,
         "roofline": roofline,
     }
@@ -190,7 +332,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, inp)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.block, ln2)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -118,6 +118,23 @@ int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle);
 int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg,
                    void* out, void* stream);
 
+/* The standard (serial) layer the parallel block replaces, built from the same
+ * kernels for comparison (MegaScale guided reading, section 2: in a standard
+ * layer the attention sub-layer runs first and the feed-forward sub-layer
+ * consumes its output; section 8, Table 3 prices the parallel form at +4.6 MFU
+ * points).  Pre-LayerNorm form:
+ *   h = x + Attn(LN1(x)),   y = h + W2 GeLU(W1 LN2(h))
+ * LN1 = (w->ln_gamma, w->ln_beta), LN2 = (ln2_gamma, ln2_beta), both [d].  The
+ * attention sub-layer uses W_in rows [0, 3*H*hd) and W_out columns [0, H*hd),
+ * the feed-forward sub-layer W_in rows [3*H*hd, 3*H*hd + ffn) and W_out columns
+ * [H*hd, H*hd + ffn): the same packed matrices as pblock_forward, so the two
+ * forms can be timed on identical parameters.  cfg->add_residual must be 1
+ * (PBLOCK_ERR_ARG otherwise).  out [B*S, d] holds h between the sub-layers.
+ * Stream, ownership, alignment, aliasing and cfg rules as pblock_forward; the
+ * LN2 parameters must be 16-byte aligned and must not overlap out. */
+int pblock_forward_serial(pblock_t h, const void* x, const pblock_weights* w, const void* ln2_gamma,
+                          const void* ln2_beta, const pblock_cfg* cfg, void* out, void* stream);
+
 /* Frees the workspace and the handle.  NULL is a no-op.  The caller must have
  * synchronised every stream the handle was used on. */
 int pblock_destroy(pblock_t h);
@@ -142,11 +159,13 @@ int pblock_intermediates(pblock_t h, void** u, void** qkv, void** ag);
  * has run on the handle. */
 int pblock_copy_intermediates(pblock_t h, void* u, void* qkv, void* ag, void* stream);
 
-/* Per-kernel timing.  When enabled, pblock_forward records HIP events around
- * each of its launches on the forward's stream; pblock_kernel_times then
- * synchronises on the last recorded event and returns the summed milliseconds
- * per kernel since the last reset, in the order [layernorm, gemm_in,
- * attention, gemm_out], plus the number of forwards timed.  Enabling or
+/* Per-kernel timing.  When enabled, pblock_forward and pblock_forward_serial
+ * record HIP events around each of their launches on the forward's stream;
+ * pblock_kernel_times then synchronises on the last recorded event and returns
+ * the summed milliseconds per kernel since the last reset, in the order
+ * [layernorm, gemm_in, attention, gemm_out], plus the number of forwards timed
+ * (the serial form's two LayerNorms count as layernorm, its QKV and FC1 GEMMs
+ * as gemm_in, its output-projection and FC2 GEMMs as gemm_out).  Enabling or
  * disabling resets the sums.  n must be >= 4. */
 int pblock_set_timing(pblock_t h, int enable);
 int pblock_kernel_times(pblock_t h, float* ms, int n, int* n_forwards);
@@ -159,6 +178,16 @@ int pblock_kernel_times(pblock_t h, float* ms, int n, int* n_forwards);
  * dtype as above; hd in {64, 128}.  Enqueued on `stream`, no sync. */
 int pblock_swa_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, int32_t B, int32_t S,
                          int32_t H, int32_t hd, int32_t W, int32_t dtype, void* stream);
+
+/* Measurement aid, not part of the block: a register-only loop of
+ * v_mfma_f32_32x32x16_bf16 (the GEMMs' instruction) on `workgroups` workgroups
+ * of 4 wavefronts, each wavefront issuing 16 independent MFMAs per iteration,
+ * `iterations` times; it performs workgroups * 4 * iterations * 16 * 32768
+ * FLOP and writes one float per thread to sink (workgroups * 256 floats, caller
+ * owned, device memory).  Timing it gives the MFMA rate the chip sustains at
+ * its present clock and power state, the ceiling the GEMMs are compared with.
+ * workgroups >= 1, iterations >= 1.  Enqueued on `stream`, no sync. */
+int pblock_mfma_loop(int32_t workgroups, int32_t iterations, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,8 @@ from .block import (  # noqa: F401
     gelu,
     layer_norm,
     relative_error,
+    serial_block_forward,
+    serial_block_forward_rows,
     split_projection,
     swa_attention,
     window_lo,

@@ -32,10 +32,16 @@ comes from scipy.  Attention is evaluated per slab of queries against only the
 keys that can fall in their windows, with an explicit band mask, so its cost
 grows with S*W rather than S^2.
 
+The serial (pre-LayerNorm) layer the parallel block replaces is here too, for
+the comparison of the two forms (section 2 contrasts them; section 8's ablation
+prices the parallel form); "standard layer" is read as the pre-LN layout.
+
 Pins (all in the CPU test-suite): dense brute-force band attention, W >= S vs
 torch's causal attention, W = 1 closed form, 2-key closed form, the branch-sum
 identity, LayerNorm and GeLU against torch and math.erf, tensor-parallel
-decomposition, locality, and hand-derived closed-form blocks.
+decomposition, locality, and hand-derived closed-form blocks; the serial layer
+against torch library routines and, with one sub-layer switched off, against
+the parallel block.
 """
 from __future__ import annotations
 
@@ -170,6 +176,57 @@ def block_forward_rows(x, gamma, beta, w_in, w_out, H: int, hd: int, W: int, row
         if add_residual:
             y = y + xs[i0 - j0:]
         outs.append(y)
+    return outs
+
+
+def serial_block_forward(x, gamma, beta, gamma2, beta2, w_in, w_out, H: int, hd: int, W: int,
+                         eps: float = 1e-5):
+    """The standard (serial) layer the parallel block replaces, in pre-LayerNorm form
+    (MegaScale guided reading, section 2: in a standard layer the attention sub-layer
+    runs first and the feed-forward sub-layer consumes its output):
+
+        h = x + Attn_SWA(LN1 x) W_o^T
+        y = h + GeLU(LN2(h) W_1^T) W_2^T
+
+    with the same packed matrices as block_forward: W_in rows [Q; K; V; W_1], W_out
+    columns [W_o ; W_2].  LN1 = (gamma, beta), LN2 = (gamma2, beta2).
+    """
+    x = np.asarray(x, np.float64)
+    w_in = np.asarray(w_in, np.float64)
+    w_out = np.asarray(w_out, np.float64)
+    B, S, d = x.shape
+    A = H * hd
+    u1 = layer_norm(x, gamma, beta, eps)
+    q, k, v, _ = split_projection(u1 @ w_in[:3 * A].T, H, hd)
+    o = np.empty((B, S, H, hd))
+    for b in range(B):
+        o[b] = swa_attention(q[b], k[b], v[b], W)
+    h = x + o.reshape(B, S, A) @ w_out[:, :A].T
+    u2 = layer_norm(h, gamma2, beta2, eps)
+    return h + gelu(u2 @ w_in[3 * A:].T) @ w_out[:, A:].T
+
+
+def serial_block_forward_rows(x, gamma, beta, gamma2, beta2, w_in, w_out, H: int, hd: int, W: int,
+                              row_blocks, eps: float = 1e-5):
+    """Output rows y[b, i0:i1] of serial_block_forward for each (b, i0, i1) in
+    ``row_blocks``, forming only the keys those queries reach.  Returns a list of
+    [i1-i0, d] arrays."""
+    w_in = np.asarray(w_in, np.float64)
+    w_out = np.asarray(w_out, np.float64)
+    A = H * hd
+    outs = []
+    for b, i0, i1 in row_blocks:
+        j0 = window_lo(i0, W)
+        xs = np.asarray(x[b, j0:i1], np.float64)
+        u1 = layer_norm(xs, gamma, beta, eps)
+        z_kv = u1 @ w_in[A:3 * A].T
+        k = z_kv[:, :A].reshape(-1, H, hd)
+        v = z_kv[:, A:].reshape(-1, H, hd)
+        q = (u1[i0 - j0:] @ w_in[:A].T).reshape(-1, H, hd)
+        o = swa_attention(q, k, v, W, q_pos0=i0, k_pos0=j0)
+        h = xs[i0 - j0:] + o.reshape(-1, A) @ w_out[:, :A].T
+        u2 = layer_norm(h, gamma2, beta2, eps)
+        outs.append(h + gelu(u2 @ w_in[3 * A:].T) @ w_out[:, A:].T)
     return outs
 
 

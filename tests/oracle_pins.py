@@ -73,6 +73,24 @@ def _torch_block(x, gamma, beta, w_in, w_out, H, hd, W, eps, add_residual=True):
     return y.numpy()
 
 
+def _torch_serial_block(x, g1, b1, g2, b2, w_in, w_out, H, hd, W, eps):
+    """The serial pre-LN layer assembled from torch float64 library routines."""
+    tx = torch.from_numpy(x)
+    A = H * hd
+    B, S, d = x.shape
+    wi = torch.from_numpy(w_in)
+    wo = torch.from_numpy(w_out)
+    u1 = F.layer_norm(tx, (d,), torch.from_numpy(g1), torch.from_numpy(b1), eps)
+    qkv = F.linear(u1, wi[:3 * A])
+    q, k, v = (qkv[..., c * A:(c + 1) * A].reshape(B, S, H, hd).transpose(1, 2) for c in range(3))
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=(j <= i) & (j > i - W)).transpose(1, 2).reshape(B, S, A)
+    h = tx + F.linear(o, wo[:, :A])
+    u2 = F.layer_norm(h, (d,), torch.from_numpy(g2), torch.from_numpy(b2), eps)
+    return (h + F.linear(F.gelu(F.linear(u2, wi[3 * A:]), approximate="none"), wo[:, A:])).numpy()
+
+
 # ----------------------------------------------------------------------------- attention
 
 
@@ -314,6 +332,56 @@ def pin_rows_match_full(ob):
         np.testing.assert_allclose(y, full[bb, i0:i1], rtol=1e-12, atol=1e-13)
 
 
+def pin_serial_vs_torch(ob):
+    """Serial pre-LN layer == the same layer assembled from torch fp64 library routines
+    (odd shapes, several windows, distinct random LN1 and LN2 parameters)."""
+    for seed, (B, S, d, H, hd, ffn), W in ((61, (2, 45, 24, 3, 8, 40), 9),
+                                           (62, (1, 70, 32, 2, 16, 48), 70),
+                                           (63, (3, 17, 16, 1, 8, 8), 1)):
+        x, g1, b1, wi, wo = _rand_block(seed, B, S, d, H, hd, ffn)
+        rng = _rng(seed + 100)
+        g2 = 1.0 + 0.3 * rng.standard_normal(d)
+        b2 = 0.2 * rng.standard_normal(d)
+        got = ob.serial_block_forward(x, g1, b1, g2, b2, wi, wo, H, hd, W)
+        ref = _torch_serial_block(x, g1, b1, g2, b2, wi, wo, H, hd, W, 1e-5)
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+
+
+def pin_serial_single_sublayer(ob):
+    """With one sub-layer switched off the serial and parallel forms coincide: W_2 = 0
+    leaves h = x + attention branch (the parallel block with FC1 rows zero); W_o = 0
+    leaves h = x and y = x + MLP(LN2 x) (the parallel block with V rows zero, LN2 = LN1).
+    With both on, they differ (LN2 sees h, not x)."""
+    B, S, d, H, hd, ffn, W = 2, 40, 32, 2, 8, 48, 11
+    x, g, b, wi, wo = _rand_block(71, B, S, d, H, hd, ffn)
+    A = H * hd
+    wo_attn = wo.copy()
+    wo_attn[:, A:] = 0
+    wi_attn = wi.copy()
+    wi_attn[3 * A:] = 0
+    np.testing.assert_allclose(ob.serial_block_forward(x, g, b, g, b, wi, wo_attn, H, hd, W),
+                               ob.block_forward(x, g, b, wi_attn, wo, H, hd, W), rtol=1e-11, atol=1e-12)
+    wo_mlp = wo.copy()
+    wo_mlp[:, :A] = 0
+    wi_mlp = wi.copy()
+    wi_mlp[2 * A:3 * A] = 0
+    np.testing.assert_allclose(ob.serial_block_forward(x, g, b, g, b, wi, wo_mlp, H, hd, W),
+                               ob.block_forward(x, g, b, wi_mlp, wo, H, hd, W), rtol=1e-11, atol=1e-12)
+    both = ob.serial_block_forward(x, g, b, g, b, wi, wo, H, hd, W)
+    assert np.abs(both - ob.block_forward(x, g, b, wi, wo, H, hd, W)).max() > 1e-3
+
+
+def pin_serial_rows_match_full(ob):
+    """serial_block_forward_rows == slices of serial_block_forward."""
+    B, S, d, H, hd, ffn, W = 2, 90, 24, 3, 8, 40, 13
+    x, g1, b1, wi, wo = _rand_block(81, B, S, d, H, hd, ffn)
+    g2, b2 = g1[::-1].copy(), b1[::-1].copy()
+    full = ob.serial_block_forward(x, g1, b1, g2, b2, wi, wo, H, hd, W)
+    blocks = [(0, 0, 5), (1, 7, 30), (0, 60, 90), (1, 89, 90)]
+    for (b, i0, i1), y in zip(blocks, ob.serial_block_forward_rows(x, g1, b1, g2, b2, wi, wo, H, hd, W, blocks)):
+        np.testing.assert_allclose(y, full[b, i0:i1], rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [
     pin_attention_brute_force,
     pin_attention_vs_torch_band,
@@ -330,4 +398,7 @@ ALL_PINS = [
     pin_block_locality,
     pin_block_uniform_closed_form,
     pin_rows_match_full,
+    pin_serial_vs_torch,
+    pin_serial_single_sublayer,
+    pin_serial_rows_match_full,
 ]

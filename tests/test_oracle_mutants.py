@@ -38,6 +38,12 @@ MUTANTS = {
     "residual_of_ln_output": [("        y = y + x\n", "        y = y + u\n")],
     "w_out_not_transposed": [("y = ag @ w_out.T", "y = ag @ w_out.reshape(w_out.shape[1], w_out.shape[0])")],
     "softmax_over_all_keys": [("scores = np.where(allowed[None], scores, -np.inf)", "scores = scores")],
+    "serial_ln2_on_x": [("u2 = layer_norm(h, gamma2, beta2, eps)\n    return h +",
+                         "u2 = layer_norm(x, gamma2, beta2, eps)\n    return h +")],
+    "serial_ln2_uses_ln1_params": [("layer_norm(h, gamma2, beta2, eps)", "layer_norm(h, gamma, beta, eps)")],
+    "serial_no_inner_residual": [("h = x + o.reshape(B, S, A) @ w_out[:, :A].T", "h = o.reshape(B, S, A) @ w_out[:, :A].T")],
+    "serial_mlp_residual_from_x": [("    return h + gelu(u2 @ w_in[3 * A:].T) @ w_out[:, A:].T",
+                                    "    return x + gelu(u2 @ w_in[3 * A:].T) @ w_out[:, A:].T")],
 }
 
 

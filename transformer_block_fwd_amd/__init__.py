@@ -126,6 +126,32 @@ def pblock_forward(handle: int, x, weights, cfg, out, stream=None) -> None:
                                          _ptr(out), _stream(stream)), "pblock_forward")
 
 
+def pblock_forward_serial(handle: int, x, weights, ln2, cfg, out, stream=None) -> None:
+    """The serial (pre-LN) layer from the same kernels: weights = (ln_gamma, ln_beta, w_in, w_out) as for
+    pblock_forward, ln2 = (ln2_gamma, ln2_beta)."""
+    c = as_cfg(cfg)
+    gamma, beta, w_in, w_out = weights
+    gamma2, beta2 = ln2
+    M, A = c.B * c.S, c.H * c.hd
+    for t, name, n in ((x, "x", M * c.d), (out, "out", M * c.d), (gamma, "ln_gamma", c.d), (beta, "ln_beta", c.d),
+                       (gamma2, "ln2_gamma", c.d), (beta2, "ln2_beta", c.d),
+                       (w_in, "w_in", (3 * A + c.ffn) * c.d), (w_out, "w_out", c.d * (A + c.ffn))):
+        _check_tensor(t, name, c.dtype, n)
+    w = PblockWeights(_ptr(gamma), _ptr(beta), _ptr(w_in), _ptr(w_out))
+    _abi.check(_abi.lib().pblock_forward_serial(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), _ptr(gamma2),
+                                                _ptr(beta2), ctypes.byref(c), _ptr(out), _stream(stream)),
+               "pblock_forward_serial")
+
+
+def pblock_mfma_loop(workgroups: int, iterations: int, sink, stream=None) -> None:
+    """Measurement aid: register-only MFMA loop, workgroups * 4 * iterations * 16 * 32768 FLOP; sink is a
+    float32 GPU tensor of at least workgroups * 256 elements."""
+    if sink.dtype.itemsize != 4 or sink.numel() < workgroups * 256 or not sink.is_cuda:
+        raise ValueError("sink must be a float32 GPU tensor of at least workgroups * 256 elements")
+    _abi.check(_abi.lib().pblock_mfma_loop(int(workgroups), int(iterations), _ptr(sink), _stream(stream)),
+               "pblock_mfma_loop")
+
+
 def pblock_intermediates(handle: int) -> tuple[int, int, int]:
     u, qkv, ag = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
     _abi.check(_abi.lib().pblock_intermediates(ctypes.c_void_p(handle), ctypes.byref(u), ctypes.byref(qkv),

@@ -127,6 +127,49 @@ int launch_status(const char* what) {
   return PBLOCK_OK;
 }
 
+// Register-only MFMA loop (measurement aid): operands drawn from the thread id by an
+// integer hash so the datapath sees non-trivial bf16 values.
+__global__ __launch_bounds__(256, 1) void mfma_loop_kernel(int iters, float* sink) {
+  const uint32_t s = blockIdx.x * 256u + threadIdx.x;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 ua, ub;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t h = (s * 8u + uint32_t(i) * 4u + uint32_t(e)) * 2654435761u;
+      h ^= h >> 15;
+      h *= 0x2c1b3c6du;
+      h ^= h >> 12;
+      ua[e] = h & 0x3F7F3F7Fu;  // two bf16 values in (-2, 2)
+      ub[e] = (h >> 1) & 0x3F7F3F7Fu;
+    }
+    a[i] = __builtin_bit_cast(bf16x8, ua);
+    b[i] = __builtin_bit_cast(bf16x8, ub);
+  }
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t += acc[i][j][r];
+  sink[s] = t;
+}
+
 // ------------------------------------------------------------------------ launches
 
 template <typename T>
@@ -209,8 +252,16 @@ void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, in
   }
 }
 
-constexpr int kTimedKernels = 4;
+constexpr int kTimedKernels = 4;  // categories: layernorm, gemm_in, attention, gemm_out
+constexpr int kMaxLaunches = 8;   // launches of one forward that get their own event pair
 constexpr size_t kEventPool = 256;
+
+// Events of one timed forward: ev[k] .. ev[k+1] brackets launch k, of category cat[k].
+struct EventSet {
+  std::array<hipEvent_t, kMaxLaunches + 1> ev;
+  int n;
+  int cat[kMaxLaunches];
+};
 
 }  // namespace
 
@@ -223,7 +274,7 @@ struct pblock_s {
   void* ws;
   WsLayout lay;
   bool timing;
-  std::vector<std::array<hipEvent_t, kTimedKernels + 1>> events;
+  std::vector<EventSet> events;
   size_t ev_used;
   double ms_sum[kTimedKernels];
   int n_forwards;
@@ -233,7 +284,7 @@ namespace {
 
 void destroy_events(pblock_s* h) {
   for (auto& set : h->events)
-    for (auto e : set) (void)hipEventDestroy(e);
+    for (auto e : set.ev) (void)hipEventDestroy(e);
   h->events.clear();
   h->ev_used = 0;
 }
@@ -241,18 +292,143 @@ void destroy_events(pblock_s* h) {
 int drain_events(pblock_s* h) {
   for (size_t i = 0; i < h->ev_used; ++i) {
     auto& set = h->events[i];
-    hipError_t e = hipEventSynchronize(set[kTimedKernels]);
+    hipError_t e = hipEventSynchronize(set.ev[set.n]);
     if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
-    for (int k = 0; k < kTimedKernels; ++k) {
+    for (int k = 0; k < set.n; ++k) {
       float ms = 0.f;
-      e = hipEventElapsedTime(&ms, set[k], set[k + 1]);
+      e = hipEventElapsedTime(&ms, set.ev[k], set.ev[k + 1]);
       if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipEventElapsedTime: ") + hipGetErrorString(e));
-      h->ms_sum[k] += ms;
+      h->ms_sum[set.cat[k]] += ms;
     }
     h->n_forwards += 1;
   }
   h->ev_used = 0;
   return PBLOCK_OK;
+}
+
+// Argument checks shared by both block forms (all before any launch).
+int check_forward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out, Dims* dm_out) {
+  if (!h) return fail(PBLOCK_ERR_NULL, "handle is NULL");
+  if (!x || !w || !out || !w->ln_gamma || !w->ln_beta || !w->w_in || !w->w_out)
+    return fail(PBLOCK_ERR_NULL, "x, out, weights or a weight pointer is NULL");
+  int st = validate(cfg);
+  if (st != PBLOCK_OK) return st;
+  const pblock_cfg& c = *cfg;
+  const pblock_cfg& hc = h->cfg;
+  if (c.d != hc.d || c.H != hc.H || c.hd != hc.hd || c.ffn != hc.ffn || c.dtype != hc.dtype)
+    return fail(PBLOCK_ERR_CFG_MISMATCH, "d, H, hd, ffn and dtype must equal the handle's");
+  const Dims dm = dims(&c);
+  if (dm.M > h->m_cap) return fail(PBLOCK_ERR_CFG_MISMATCH, "B*S exceeds the handle's B*S");
+  if (!aligned16(x) || !aligned16(out) || !aligned16(w->ln_gamma) || !aligned16(w->ln_beta) ||
+      !aligned16(w->w_in) || !aligned16(w->w_out))
+    return fail(PBLOCK_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const int es = elem_size(c.dtype);
+  const int64_t xb = dm.M * c.d * es;
+  if (overlap(out, xb, x, xb) || overlap(out, xb, w->w_in, dm.n_in * c.d * es) ||
+      overlap(out, xb, w->w_out, int64_t(c.d) * dm.k_out * es) || overlap(out, xb, w->ln_gamma, c.d * es) ||
+      overlap(out, xb, w->ln_beta, c.d * es))
+    return fail(PBLOCK_ERR_ALIAS, "out overlaps x or a weight");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev != h->device) return fail(PBLOCK_ERR_DEVICE, "current device differs from the handle's");
+  *dm_out = dm;
+  return PBLOCK_OK;
+}
+
+struct Ws {
+  void *u, *qkv, *ag;
+  SkScratch scr;
+};
+Ws workspace(pblock_s* h) {
+  char* base = static_cast<char*>(h->ws);
+  Ws w;
+  w.u = base + h->lay.u;
+  w.qkv = base + h->lay.qkv;
+  w.ag = base + h->lay.ag;
+  w.scr.partials = reinterpret_cast<float*>(base + h->lay.partials);
+  w.scr.G = h->n_cu;
+  return w;
+}
+
+// HIP events around the launches of one forward when the handle's timing is on.
+struct Timer {
+  EventSet* set = nullptr;
+  hipStream_t s = nullptr;
+  int begin(pblock_s* h, hipStream_t stream) {
+    s = stream;
+    if (!h->timing) return PBLOCK_OK;
+    if (h->ev_used == h->events.size()) {
+      int st = drain_events(h);
+      if (st != PBLOCK_OK) return st;
+    }
+    set = &h->events[h->ev_used++];
+    set->n = 0;
+    (void)hipEventRecord(set->ev[0], s);
+    return PBLOCK_OK;
+  }
+  void mark(int category) {
+    if (!set || set->n >= kMaxLaunches) return;
+    set->cat[set->n] = category;
+    (void)hipEventRecord(set->ev[++set->n], s);
+  }
+};
+
+void run_layernorm(const void* x, const void* g, const void* b, void* u, int64_t M, const pblock_cfg& c, hipStream_t s) {
+  if (c.dtype == PBLOCK_BF16)
+    launch_layernorm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(b),
+                     static_cast<uint16_t*>(u), M, c.d, c.ln_eps, s);
+  else
+    launch_layernorm(static_cast<const float*>(x), static_cast<const float*>(g), static_cast<const float*>(b),
+                     static_cast<float*>(u), M, c.d, c.ln_eps, s);
+}
+
+// out0[m, n] = Z[m, n] for n < nsplit; out1[m, off1 + n - nsplit] = GeLU(Z[m, n]) otherwise;
+// Z = A B^T, A [M, K] (row stride lda), B [N, K] (row stride ldb).
+void run_gemm_in(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M, int64_t N, int64_t K, void* out0,
+                 int64_t ld0, void* out1, int64_t ld1, int64_t off1, int64_t nsplit, int dtype, const SkScratch& scr,
+                 hipStream_t s) {
+  if (dtype == PBLOCK_BF16) {
+    GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(a); g.lda = lda;
+    g.b = static_cast<const uint16_t*>(b); g.ldb = ldb;
+    g.M = int(M); g.N = int(N); g.K = int(K);
+    g.out0 = static_cast<uint16_t*>(out0); g.ld0 = ld0;
+    g.out1 = static_cast<uint16_t*>(out1); g.ld1 = ld1; g.off1 = off1;
+    g.nsplit = int(nsplit);
+    launch_gemm_bf16<kEpiSplitGelu>(g, scr, s);
+  } else {
+    GemmArgsF32 g{};
+    g.a = static_cast<const float*>(a); g.lda = lda;
+    g.b = static_cast<const float*>(b); g.ldb = ldb;
+    g.M = int(M); g.N = int(N); g.K = int(K);
+    g.out0 = static_cast<float*>(out0); g.ld0 = ld0;
+    g.out1 = static_cast<float*>(out1); g.ld1 = ld1; g.off1 = off1;
+    g.nsplit = int(nsplit);
+    launch_gemm_f32<kEpiSplitGelu>(g, s);
+  }
+}
+
+// out [M, N] (row stride N) = A B^T (+ resid [M, N], row stride N); resid may be out itself
+// (each element is read by the thread that then writes it).
+void run_gemm_out(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M, int64_t N, int64_t K, void* out,
+                  const void* resid, int dtype, const SkScratch& scr, hipStream_t s) {
+  if (dtype == PBLOCK_BF16) {
+    GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(a); g.lda = lda;
+    g.b = static_cast<const uint16_t*>(b); g.ldb = ldb;
+    g.M = int(M); g.N = int(N); g.K = int(K);
+    g.out0 = static_cast<uint16_t*>(out); g.ld0 = N;
+    g.resid = static_cast<const uint16_t*>(resid); g.ldr = N;
+    launch_gemm_bf16<kEpiResidual>(g, scr, s);
+  } else {
+    GemmArgsF32 g{};
+    g.a = static_cast<const float*>(a); g.lda = lda;
+    g.b = static_cast<const float*>(b); g.ldb = ldb;
+    g.M = int(M); g.N = int(N); g.K = int(K);
+    g.out0 = static_cast<float*>(out); g.ld0 = N;
+    g.resid = static_cast<const float*>(resid); g.ldr = N;
+    launch_gemm_f32<kEpiResidual>(g, s);
+  }
 }
 
 }  // namespace
@@ -365,7 +541,7 @@ int pblock_set_timing(pblock_t h, int enable) {
     if (h->timing) {
       h->events.resize(kEventPool);
       for (auto& set : h->events)
-        for (auto& ev : set) {
+        for (auto& ev : set.ev) {
           hipError_t e = hipEventCreate(&ev);
           if (e != hipSuccess) {
             h->timing = false;
@@ -392,102 +568,79 @@ int pblock_kernel_times(pblock_t h, float* ms, int n, int* n_forwards) {
 int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out,
                    void* stream) {
   try {
-    if (!h) return fail(PBLOCK_ERR_NULL, "handle is NULL");
-    if (!x || !w || !out || !w->ln_gamma || !w->ln_beta || !w->w_in || !w->w_out)
-      return fail(PBLOCK_ERR_NULL, "x, out, weights or a weight pointer is NULL");
-    int st = validate(cfg);
+    Dims dm;
+    int st = check_forward(h, x, w, cfg, out, &dm);
     if (st != PBLOCK_OK) return st;
     const pblock_cfg& c = *cfg;
-    const pblock_cfg& hc = h->cfg;
-    if (c.d != hc.d || c.H != hc.H || c.hd != hc.hd || c.ffn != hc.ffn || c.dtype != hc.dtype)
-      return fail(PBLOCK_ERR_CFG_MISMATCH, "d, H, hd, ffn and dtype must equal the handle's");
-    const Dims dm = dims(&c);
-    if (dm.M > h->m_cap) return fail(PBLOCK_ERR_CFG_MISMATCH, "B*S exceeds the handle's B*S");
-    if (!aligned16(x) || !aligned16(out) || !aligned16(w->ln_gamma) || !aligned16(w->ln_beta) ||
-        !aligned16(w->w_in) || !aligned16(w->w_out))
-      return fail(PBLOCK_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-    const int es = elem_size(c.dtype);
-    const int64_t xb = dm.M * c.d * es;
-    if (overlap(out, xb, x, xb) || overlap(out, xb, w->w_in, dm.n_in * c.d * es) ||
-        overlap(out, xb, w->w_out, int64_t(c.d) * dm.k_out * es) || overlap(out, xb, w->ln_gamma, c.d * es) ||
-        overlap(out, xb, w->ln_beta, c.d * es))
-      return fail(PBLOCK_ERR_ALIAS, "out overlaps x or a weight");
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess || dev != h->device) return fail(PBLOCK_ERR_DEVICE, "current device differs from the handle's");
-
     hipStream_t s = static_cast<hipStream_t>(stream);
-    char* base = static_cast<char*>(h->ws);
-    void* u = base + h->lay.u;
-    void* qkv = base + h->lay.qkv;
-    void* ag = base + h->lay.ag;
-    SkScratch scr;
-    scr.partials = reinterpret_cast<float*>(base + h->lay.partials);
-    scr.G = h->n_cu;
+    const Ws ws = workspace(h);
+    Timer tm;
+    st = tm.begin(h, s);
+    if (st != PBLOCK_OK) return st;
+    const int64_t A = dm.A;
 
-    std::array<hipEvent_t, kTimedKernels + 1>* ev = nullptr;
-    if (h->timing) {
-      if (h->ev_used == h->events.size()) {
-        st = drain_events(h);
-        if (st != PBLOCK_OK) return st;
-      }
-      ev = &h->events[h->ev_used++];
-      (void)hipEventRecord((*ev)[0], s);
-    }
-
-    if (c.dtype == PBLOCK_BF16) {
-      launch_layernorm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->ln_gamma),
-                       static_cast<const uint16_t*>(w->ln_beta), static_cast<uint16_t*>(u), dm.M, c.d, c.ln_eps, s);
-    } else {
-      launch_layernorm(static_cast<const float*>(x), static_cast<const float*>(w->ln_gamma),
-                       static_cast<const float*>(w->ln_beta), static_cast<float*>(u), dm.M, c.d, c.ln_eps, s);
-    }
-    if (ev) (void)hipEventRecord((*ev)[1], s);
-
-    if (c.dtype == PBLOCK_BF16) {
-      GemmArgs g{};
-      g.a = static_cast<const uint16_t*>(u); g.lda = c.d;
-      g.b = static_cast<const uint16_t*>(w->w_in); g.ldb = c.d;
-      g.M = int(dm.M); g.N = int(dm.n_in); g.K = c.d;
-      g.out0 = static_cast<uint16_t*>(qkv); g.ld0 = 3 * dm.A;
-      g.out1 = static_cast<uint16_t*>(ag); g.ld1 = dm.k_out; g.off1 = dm.A;
-      g.nsplit = int(3 * dm.A);
-      launch_gemm_bf16<kEpiSplitGelu>(g, scr, s);
-    } else {
-      GemmArgsF32 g{};
-      g.a = static_cast<const float*>(u); g.lda = c.d;
-      g.b = static_cast<const float*>(w->w_in); g.ldb = c.d;
-      g.M = int(dm.M); g.N = int(dm.n_in); g.K = c.d;
-      g.out0 = static_cast<float*>(qkv); g.ld0 = 3 * dm.A;
-      g.out1 = static_cast<float*>(ag); g.ld1 = dm.k_out; g.off1 = dm.A;
-      g.nsplit = int(3 * dm.A);
-      launch_gemm_f32<kEpiSplitGelu>(g, s);
-    }
-    if (ev) (void)hipEventRecord((*ev)[2], s);
-
-    launch_attention(qkv, 3 * dm.A, ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
-    if (ev) (void)hipEventRecord((*ev)[3], s);
-
-    if (c.dtype == PBLOCK_BF16) {
-      GemmArgs g{};
-      g.a = static_cast<const uint16_t*>(ag); g.lda = dm.k_out;
-      g.b = static_cast<const uint16_t*>(w->w_out); g.ldb = dm.k_out;
-      g.M = int(dm.M); g.N = c.d; g.K = int(dm.k_out);
-      g.out0 = static_cast<uint16_t*>(out); g.ld0 = c.d;
-      g.resid = c.add_residual ? static_cast<const uint16_t*>(x) : nullptr; g.ldr = c.d;
-      launch_gemm_bf16<kEpiResidual>(g, scr, s);
-    } else {
-      GemmArgsF32 g{};
-      g.a = static_cast<const float*>(ag); g.lda = dm.k_out;
-      g.b = static_cast<const float*>(w->w_out); g.ldb = dm.k_out;
-      g.M = int(dm.M); g.N = c.d; g.K = int(dm.k_out);
-      g.out0 = static_cast<float*>(out); g.ld0 = c.d;
-      g.resid = c.add_residual ? static_cast<const float*>(x) : nullptr; g.ldr = c.d;
-      launch_gemm_f32<kEpiResidual>(g, s);
-    }
-    if (ev) (void)hipEventRecord((*ev)[4], s);
+    run_layernorm(x, w->ln_gamma, w->ln_beta, ws.u, dm.M, c, s);
+    tm.mark(0);
+    // Z = u W_in^T: Q|K|V columns to QKV, FC1 columns through GeLU to AG[:, A:]
+    run_gemm_in(ws.u, c.d, w->w_in, c.d, dm.M, dm.n_in, c.d, ws.qkv, 3 * A, ws.ag, dm.k_out, A, 3 * A, c.dtype, ws.scr,
+                s);
+    tm.mark(1);
+    launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
+    tm.mark(2);
+    // y = [attention | GeLU] W_out^T (+ x): both branches summed in one accumulator
+    run_gemm_out(ws.ag, dm.k_out, w->w_out, dm.k_out, dm.M, c.d, dm.k_out, out, c.add_residual ? x : nullptr, c.dtype,
+                 ws.scr, s);
+    tm.mark(3);
     h->last_m = dm.M;
     return launch_status("pblock_forward launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int pblock_forward_serial(pblock_t h, const void* x, const pblock_weights* w, const void* ln2_gamma,
+                          const void* ln2_beta, const pblock_cfg* cfg, void* out, void* stream) {
+  try {
+    Dims dm;
+    int st = check_forward(h, x, w, cfg, out, &dm);
+    if (st != PBLOCK_OK) return st;
+    const pblock_cfg& c = *cfg;
+    if (!ln2_gamma || !ln2_beta) return fail(PBLOCK_ERR_NULL, "ln2_gamma or ln2_beta is NULL");
+    if (!aligned16(ln2_gamma) || !aligned16(ln2_beta)) return fail(PBLOCK_ERR_ALIGN, "LN2 parameters must be 16-byte aligned");
+    const int es = elem_size(c.dtype);
+    const int64_t xb = dm.M * c.d * es;
+    if (overlap(out, xb, ln2_gamma, c.d * es) || overlap(out, xb, ln2_beta, c.d * es))
+      return fail(PBLOCK_ERR_ALIAS, "out overlaps an LN2 parameter");
+    if (!c.add_residual) return fail(PBLOCK_ERR_ARG, "the serial form needs add_residual = 1 (its residual stream)");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Ws ws = workspace(h);
+    Timer tm;
+    st = tm.begin(h, s);
+    if (st != PBLOCK_OK) return st;
+    const int64_t A = dm.A;
+    const char* w_in = static_cast<const char*>(w->w_in);
+    const char* w_out = static_cast<const char*>(w->w_out);
+    char* ag = static_cast<char*>(ws.ag);
+
+    // attention sub-layer: h = x + Attn(LN1(x)), h kept in out
+    run_layernorm(x, w->ln_gamma, w->ln_beta, ws.u, dm.M, c, s);
+    tm.mark(0);
+    run_gemm_in(ws.u, c.d, w_in, c.d, dm.M, 3 * A, c.d, ws.qkv, 3 * A, nullptr, 0, 0, 3 * A, c.dtype, ws.scr, s);
+    tm.mark(1);
+    launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
+    tm.mark(2);
+    run_gemm_out(ws.ag, dm.k_out, w_out, dm.k_out, dm.M, c.d, A, out, x, c.dtype, ws.scr, s);
+    tm.mark(3);
+    // feed-forward sub-layer on h: y = h + W2 GeLU(W1 LN2(h)), the residual read from out in place
+    run_layernorm(out, ln2_gamma, ln2_beta, ws.u, dm.M, c, s);
+    tm.mark(0);
+    run_gemm_in(ws.u, c.d, w_in + 3 * A * c.d * es, c.d, dm.M, c.ffn, c.d, nullptr, 0, ws.ag, dm.k_out, A, 0, c.dtype,
+                ws.scr, s);
+    tm.mark(1);
+    run_gemm_out(ag + A * es, dm.k_out, w_out + A * es, dm.k_out, dm.M, c.d, c.ffn, out, out, c.dtype, ws.scr, s);
+    tm.mark(3);
+    h->last_m = dm.M;
+    return launch_status("pblock_forward_serial launch");
   } catch (...) {
     return fail(PBLOCK_ERR_ARG, "internal error");
   }
@@ -536,5 +689,19 @@ const char* pblock_strerror(int code) {
 }
 
 const char* pblock_last_error(void) { return g_last_error.c_str(); }
+
+int pblock_mfma_loop(int32_t workgroups, int32_t iterations, float* sink, void* stream) {
+  try {
+    if (!sink) return fail(PBLOCK_ERR_NULL, "sink is NULL");
+    if (workgroups < 1 || iterations < 1) return fail(PBLOCK_ERR_ARG, "workgroups and iterations must be >= 1");
+    int st = check_device(nullptr);
+    if (st != PBLOCK_OK) return st;
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3(unsigned(workgroups)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       int(iterations), sink);
+    return launch_status("pblock_mfma_loop launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
 
 }  // extern "C"

@@ -178,6 +178,25 @@ def make_inputs(cfg: BlockConfig, seed: int = 0, affine: bool = False) -> BlockI
     return BlockInputs(cfg, x, gamma, beta, w_in, w_out, bits)
 
 
+def make_ln2(cfg: BlockConfig, seed: int = 0, affine: bool = False) -> dict[str, np.ndarray]:
+    """Second LayerNorm's parameters for the serial form of the layer, drawn like the first
+    (gamma = 1, beta = 0, or N(1, 0.1^2) / N(0, 0.1^2) with ``affine``) from their own stream.
+
+    Returns float32 values exactly as the device receives them under "gamma2"/"beta2" and
+    the storage arrays the library reads under "gamma2_dev"/"beta2_dev"."""
+    rng = np.random.Generator(np.random.PCG64([seed, 2]))
+    if affine:
+        gamma = (1.0 + 0.1 * rng.standard_normal(cfg.d, dtype=np.float32)).astype(np.float32)
+        beta = (0.1 * rng.standard_normal(cfg.d, dtype=np.float32)).astype(np.float32)
+    else:
+        gamma = np.ones(cfg.d, dtype=np.float32)
+        beta = np.zeros(cfg.d, dtype=np.float32)
+    if cfg.dtype == "bf16":
+        (g, gb), (b, bb) = round_to_bf16(gamma), round_to_bf16(beta)
+        return dict(gamma2=g, beta2=b, gamma2_dev=gb, beta2_dev=bb)
+    return dict(gamma2=gamma, beta2=beta, gamma2_dev=gamma, beta2_dev=beta)
+
+
 def sample_row_blocks(cfg: BlockConfig, block: int = 32, seed: int = 1) -> list[tuple[int, int, int]]:
     """Query row blocks (b, i0, i1) for sampled checks at full size.
 
