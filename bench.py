@@ -14,7 +14,7 @@ the dominant kernel, the rate of a register-only MFMA loop measured in the same
 run, and the fp64 CPU oracle timed on the host as a baseline.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload shard175b]
-                  [--block parallel|serial] [--window W]
+                  [--block parallel|serial] [--window W] [--chunks N]
   python bench.py --sweep      # attention time against window and sequence length
 """
 from __future__ import annotations
@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--window", type=int, default=0, help="override the workload's attention window W")
     p.add_argument("--add-residual", type=int, choices=(0, 1), default=None,
                    help="override the workload's add_residual (the serial form always adds it)")
+    p.add_argument("--chunks", type=int, default=0,
+                   help="time the forward in this many position chunks (the TP/SP overlap form) with a completion "
+                        "event per chunk; per-kernel and roofline figures then come from an unchunked pass")
     p.add_argument("--cold-steps", type=int, default=10, help="cold-cache steps after the timed run (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -225,9 +228,15 @@ def main():
     stream = torch.cuda.current_stream()
     h = tb.pblock_create(cfg)
 
-    def step():
+    if args.chunks and args.block != "parallel":
+        raise SystemExit("--chunks applies to the parallel block")
+    done = [torch.cuda.Event(enable_timing=True) for _ in range(args.chunks)]
+
+    def step(chunked=bool(args.chunks)):
         if args.block == "serial":
             tb.pblock_forward_serial(h, dev["x"], weights, (dev["gamma2"], dev["beta2"]), cfg, out, stream)
+        elif chunked:
+            tb.pblock_forward_chunked(h, dev["x"], weights, cfg, out, args.chunks, None, done, stream)
         else:
             tb.pblock_forward(h, dev["x"], weights, cfg, out, stream)
 
@@ -252,6 +261,28 @@ def main():
     tb.pblock_set_timing(h, False)
     print(f"[bench] timed {args.steps} steps in {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms)", file=sys.stderr,
           flush=True)
+
+    chunking = None
+    if args.chunks:
+        # completion of each chunk's rows of out within the last timed step
+        t_done = [marks[-2].elapsed_time(e) for e in done]
+        # the same forward unchunked, with per-kernel timing, for the kernel and roofline figures
+        tb.pblock_set_timing(h, True)
+        u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_un = max(5, args.steps // 3)
+        u0.record(stream)
+        for _ in range(n_un):
+            step(chunked=False)
+        u1.record(stream)
+        torch.cuda.synchronize()
+        kernel_ms, n_fwd = tb.pblock_kernel_times(h)
+        tb.pblock_set_timing(h, False)
+        unchunked = u0.elapsed_time(u1) / n_un
+        chunking = {"chunks": args.chunks, "chunk_done_ms": [round(v, 5) for v in t_done],
+                    "unchunked_ms_per_step": round(unchunked, 5),
+                    "chunked_over_unchunked": round((ms_total / args.steps) / unchunked, 4)}
+        print(f"[bench] chunk completion (ms into the step): {[round(v, 3) for v in t_done]}", file=sys.stderr,
+              flush=True)
 
     cold = None
     if args.cold_steps > 0:
@@ -280,7 +311,7 @@ def main():
     k_avg = {k: v / max(n_fwd, 1) for k, v in kernel_ms.items()}
     g1_ms = k_avg["gemm_in"]
     g1_flops = cfg.gemm1_flops()
-    as_profiled = args.block == "parallel" and not args.window and args.add_residual is None
+    as_profiled = args.block == "parallel" and not args.window and args.add_residual is None and not args.chunks
     traffic = MEASURED_TRAFFIC_BYTES.get(cfg.name) if as_profiled else None
     roofline = {"kernel": "gemm_in (fused QKV+FC1 GEMM, GeLU epilogue)", "bound": "mfma",
                 "achieved": round(g1_flops / (g1_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -322,6 +353,7 @@ def main():
         "step_ms": {"median": round(percentile(step_ms, 0.5), 5), "p10": round(percentile(step_ms, 0.1), 5),
                     "p90": round(percentile(step_ms, 0.9), 5)},
         "cold_cache": cold,
+        "chunking": chunking,
         "mfma_loop_tflops": round(mfma_tflops, 1),
         "pct_of_mfma_loop": round(100 * tflops / mfma_tflops, 2),
         "kernels": per_kernel,

@@ -91,8 +91,9 @@ int pblock_validate_cfg(const pblock_cfg* cfg);
 
 /* Bytes of device workspace a handle for cfg allocates, or a negative status.
  * Host only.  The workspace holds the intermediates u [Mt, d], QKV [M, 3*H*hd],
- * AG [Mt, H*hd + ffn] (M = B*S; the GEMM row operands u and AG are allocated
- * in whole 256-row tiles, Mt = M rounded up to 256) and, for bf16, the GEMM
+ * AG [Mt, H*hd + ffn] (M = B*S; the GEMM row operands u and AG get M rounded
+ * up to 256 plus 256 more rows, Mt, since the GEMM reads its row operand to
+ * the end of a 256-row tile from any starting row) and, for bf16, the GEMM
  * scratch for the split-K tail wave: one fp32 256x256 partial tile per
  * compute unit (this estimate assumes 256). */
 int64_t pblock_workspace_bytes(const pblock_cfg* cfg);
@@ -134,6 +135,27 @@ int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pbl
  * LN2 parameters must be 16-byte aligned and must not overlap out. */
 int pblock_forward_serial(pblock_t h, const void* x, const pblock_weights* w, const void* ln2_gamma,
                           const void* ln2_beta, const pblock_cfg* cfg, void* out, void* stream);
+
+/* The block forward in n_chunks chunks of sequence positions, in order, for
+ * overlapping tensor/sequence-parallel communication with compute (MegaScale
+ * guided reading, section 3: the GEMMs next to an all-gather or reduce-scatter
+ * are split into chunks so that one chunk's communication overlaps the next
+ * chunk's computation).  Chunk k covers positions [k*S/n, (k+1)*S/n) (integer
+ * division) of every sequence.  For each chunk, in order, on `stream`:
+ *   if ready_events and ready_events[k] are non-NULL, wait for that hipEvent_t
+ *   (e.g. the arrival of chunk k's rows of x);
+ *   LayerNorm, the fused QKV+FC1 GEMM, attention for the chunk's queries (their
+ *   keys reach back W-1 positions into earlier chunks) and the output GEMM for
+ *   the chunk's rows;
+ *   if done_events and done_events[k] are non-NULL, record that hipEvent_t:
+ *   chunk k's rows of out are final (the piece a reduce-scatter would send).
+ * Events are created and owned by the caller.  The result equals
+ * pblock_forward's up to floating-point summation order.  1 <= n_chunks <= S
+ * (PBLOCK_ERR_ARG otherwise); other rules as pblock_forward.  Per-kernel timing
+ * does not cover this entry point. */
+int pblock_forward_chunked(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg,
+                           void* out, int32_t n_chunks, void* const* ready_events, void* const* done_events,
+                           void* stream);
 
 /* Frees the workspace and the handle.  NULL is a no-op.  The caller must have
  * synchronised every stream the handle was used on. */

@@ -74,7 +74,7 @@ def test_workspace_and_flops():
     for cfg in CONFIGS.values():
         es = 2 if cfg.dtype == "bf16" else 4
         ws = tb.pblock_workspace_bytes(cfg)
-        mt = -(-cfg.M // 256) * 256  # GEMM row operands u, AG come in whole 256-row tiles
+        mt = -(-cfg.M // 256) * 256 + 256  # GEMM row operands u, AG: whole 256-row tiles plus one
         need = es * (mt * cfg.d + cfg.M * 3 * cfg.A + mt * cfg.k_out)
         slack = 5 * 256
         if cfg.dtype == "bf16":

@@ -143,6 +143,40 @@ def pblock_forward_serial(handle: int, x, weights, ln2, cfg, out, stream=None) -
                "pblock_forward_serial")
 
 
+def _event_array(events, n, stream):
+    """ctypes array of hipEvent_t handles for torch.cuda.Event objects (None entries stay NULL)."""
+    if events is None:
+        return None
+    if len(events) != n:
+        raise ValueError(f"expected {n} events, got {len(events)}")
+    arr = (ctypes.c_void_p * n)()
+    for i, e in enumerate(events):
+        if e is None:
+            continue
+        if not e.cuda_event:  # torch creates the underlying event at its first record
+            e.record()
+        arr[i] = e.cuda_event
+    return arr
+
+
+def pblock_forward_chunked(handle: int, x, weights, cfg, out, n_chunks: int, ready_events=None, done_events=None,
+                           stream=None) -> None:
+    """The block in n_chunks position chunks; ready_events / done_events: lists of torch.cuda.Event (or None)
+    waited on before / recorded after each chunk."""
+    c = as_cfg(cfg)
+    gamma, beta, w_in, w_out = weights
+    M, A = c.B * c.S, c.H * c.hd
+    for t, name, n in ((x, "x", M * c.d), (out, "out", M * c.d), (gamma, "ln_gamma", c.d), (beta, "ln_beta", c.d),
+                       (w_in, "w_in", (3 * A + c.ffn) * c.d), (w_out, "w_out", c.d * (A + c.ffn))):
+        _check_tensor(t, name, c.dtype, n)
+    w = PblockWeights(_ptr(gamma), _ptr(beta), _ptr(w_in), _ptr(w_out))
+    ready = _event_array(ready_events, n_chunks, stream)
+    done = _event_array(done_events, n_chunks, stream)
+    _abi.check(_abi.lib().pblock_forward_chunked(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), ctypes.byref(c),
+                                                 _ptr(out), int(n_chunks), ready, done, _stream(stream)),
+               "pblock_forward_chunked")
+
+
 def pblock_mfma_loop(workgroups: int, iterations: int, sink, stream=None) -> None:
     """Measurement aid: register-only MFMA loop, workgroups * 4 * iterations * 16 * 32768 FLOP; sink is a
     float32 GPU tensor of at least workgroups * 256 elements."""

@@ -81,6 +81,9 @@ _SIGNATURES = {
     "pblock_forward_serial": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.c_void_p,
                                          _c.c_void_p, _c.POINTER(PblockCfg), _c.c_void_p, _c.c_void_p]),
     "pblock_mfma_loop": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
+    "pblock_forward_chunked": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.POINTER(PblockCfg),
+                                          _c.c_void_p, _c.c_int32, _c.POINTER(_c.c_void_p),
+                                          _c.POINTER(_c.c_void_p), _c.c_void_p]),
 }
 
 _lib = None

@@ -10,7 +10,8 @@
 // Work decomposition: one workgroup = one (sequence, head, 128-query tile),
 // four wavefronts of 32 queries each, key/value tiles of 64.  Query tiles are
 // dispatched last-first so that, for long causal windows, the longest tiles
-// start first.
+// start first.  A launch may cover only the query positions [q_lo, q_hi) of
+// each sequence (keys still reach back W-1 positions before q_lo).
 //
 // Data movement: K and V tiles are copied global -> LDS by the load unit
 // (global_load_lds, 16 bytes per lane, 1 KiB per wave instruction) into two
@@ -43,6 +44,7 @@ struct AttnArgs {
   uint16_t* o;          // [B*S, ld_o]: head h at columns [h*hd, (h+1)*hd)
   int64_t ld_o;
   int B, S, H, W;
+  int q_lo, q_hi;       // query positions [q_lo, q_hi) of every sequence (0, S for all)
   float scale_log2;     // log2(e) / sqrt(hd)
 };
 
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
   __shared__ __attribute__((aligned(1024))) uint8_t v_st1[TB];
 
   const int S = a.S, W = a.W;
-  const int nqt = (S + BQ - 1) / BQ;
+  const int nqt = (a.q_hi - a.q_lo + BQ - 1) / BQ;
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int qt = nqt - 1 - blockIdx.x / BH;
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy targets in SGPRs
   const int lr = lane & 31, lg = lane >> 5;
-  const int q0 = qt * BQ;
+  const int q0 = a.q_lo + qt * BQ;
   const int wq0 = q0 + wave * 32;
   const int my_q = wq0 + lr;
 
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
   }
 
-  const int q_last = min(q0 + BQ, S) - 1;
+  const int q_last = min(q0 + BQ, a.q_hi) - 1;
   const int t_begin = max(0, q0 - W + 1) / BKV;
   const int t_end = q_last / BKV;
 
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
 
   auto compute = [&](int t, const uint8_t* ks, const uint8_t* vs) {
     const int j0 = t * BKV;
-    const bool active = (wq0 < S) && (j0 <= wq0 + 31) && (j0 + BKV - 1 >= wq0 - W + 1);
+    const bool active = (wq0 < a.q_hi) && (j0 <= wq0 + 31) && (j0 + BKV - 1 >= wq0 - W + 1);
     if (!active) return;
     f32x16 sacc[2];
 #pragma unroll
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
   if (n_tiles & 1) step(t, k_st0, v_st0, k_st1, v_st1);
 
   const float l = l_part + other_half(l_part);
-  if (my_q < S) {
+  if (my_q < a.q_hi) {
     const float inv = 1.0f / l;
     uint16_t* orow = a.o + (int64_t(b) * S + my_q) * a.ld_o + h * HD;
 #pragma unroll

@@ -1,7 +1,7 @@
 // Sliding-window causal attention for the fp32 debug path: one thread per
 // query walks its window j = max(0, i-W+1) .. i with an online softmax in
 // fp32 (accurate expf).  Untimed; it exists to check the block at fp32
-// tolerance.
+// tolerance.  A launch covers query positions [q_lo, q_hi) of each sequence.
 #pragma once
 
 #include "common.hpp"
@@ -11,13 +11,13 @@ namespace pblk {
 template <int HD>
 __global__ __launch_bounds__(64) void swa_attn_f32_kernel(const float* __restrict__ qkv, int64_t ld_qkv,
                                                           float* __restrict__ o, int64_t ld_o, int S, int H,
-                                                          int W, float scale) {
-  const int nqb = (S + 63) / 64;
+                                                          int W, float scale, int q_lo, int q_hi) {
+  const int nqb = (q_hi - q_lo + 63) / 64;
   const int qb = blockIdx.x % nqb;
   const int h = (blockIdx.x / nqb) % H;
   const int b = blockIdx.x / (nqb * H);
-  const int i = qb * 64 + threadIdx.x;
-  if (i >= S) return;
+  const int i = q_lo + qb * 64 + threadIdx.x;
+  if (i >= q_hi) return;
   const int A = H * HD;
   const float* base = qkv + int64_t(b) * S * ld_qkv + h * HD;
   float q[HD], acc[HD];

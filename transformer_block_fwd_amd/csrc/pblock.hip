@@ -78,9 +78,10 @@ WsLayout ws_layout(const pblock_cfg* c, int G) {
   const Dims dm = dims(c);
   const int es = elem_size(c->dtype);
   if (G <= 0) G = 256;
-  // u and ag are the GEMMs' row operands: allocated in whole 256-row tiles, since the bf16
-  // GEMM reads its A operand up to the end of the last tile (rows past M are never stored)
-  const int64_t m_tiles = (dm.M + kGemmBM - 1) / kGemmBM * kGemmBM;
+  // u and ag are the GEMMs' row operands: the bf16 GEMM reads its A operand up to the end of
+  // the last 256-row tile it covers (rows past M are never stored), and a row-chunked
+  // forward starts GEMMs at any row, so both get M rounded up to 256 plus one more tile
+  const int64_t m_tiles = (dm.M + kGemmBM - 1) / kGemmBM * kGemmBM + kGemmBM;
   WsLayout w;
   w.u = 0;
   w.qkv = align256(m_tiles * c->d * es);
@@ -229,8 +230,10 @@ void launch_gemm_f32(const GemmArgsF32& g, hipStream_t s) {
   hipLaunchKernelGGL((gemm_f32_kernel<EPI>), dim3(grid), dim3(256), 0, s, g);
 }
 
+// Attention for query positions [q_lo, q_hi) of each of the B sequences.
 void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, int B, int S, int H, int hd, int W,
-                      int dtype, hipStream_t s) {
+                      int dtype, hipStream_t s, int q_lo = 0, int q_hi = -1) {
+  if (q_hi < 0) q_hi = S;
   const float scale = 1.0f / std::sqrt(float(hd));
   if (dtype == PBLOCK_BF16) {
     AttnArgs a;
@@ -239,16 +242,19 @@ void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, in
     a.o = static_cast<uint16_t*>(o);
     a.ld_o = ld_o;
     a.B = B; a.S = S; a.H = H; a.W = W;
+    a.q_lo = q_lo; a.q_hi = q_hi;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const unsigned grid = unsigned(((S + kAttnBQ - 1) / kAttnBQ) * int64_t(B) * H);
+    const unsigned grid = unsigned(((q_hi - q_lo + kAttnBQ - 1) / kAttnBQ) * int64_t(B) * H);
     if (hd == 128) hipLaunchKernelGGL((swa_attn_bf16_kernel<128>), dim3(grid), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((swa_attn_bf16_kernel<64>), dim3(grid), dim3(256), 0, s, a);
   } else {
-    const dim3 grid{unsigned(int64_t((S + 63) / 64) * H * B)};
+    const dim3 grid{unsigned(int64_t((q_hi - q_lo + 63) / 64) * H * B)};
     const float* q = static_cast<const float*>(qkv);
     float* out = static_cast<float*>(o);
-    if (hd == 128) hipLaunchKernelGGL((swa_attn_f32_kernel<128>), grid, dim3(64), 0, s, q, ld_qkv, out, ld_o, S, H, W, scale);
-    else hipLaunchKernelGGL((swa_attn_f32_kernel<64>), grid, dim3(64), 0, s, q, ld_qkv, out, ld_o, S, H, W, scale);
+    if (hd == 128)
+      hipLaunchKernelGGL((swa_attn_f32_kernel<128>), grid, dim3(64), 0, s, q, ld_qkv, out, ld_o, S, H, W, scale, q_lo, q_hi);
+    else
+      hipLaunchKernelGGL((swa_attn_f32_kernel<64>), grid, dim3(64), 0, s, q, ld_qkv, out, ld_o, S, H, W, scale, q_lo, q_hi);
   }
 }
 
@@ -641,6 +647,58 @@ int pblock_forward_serial(pblock_t h, const void* x, const pblock_weights* w, co
     tm.mark(3);
     h->last_m = dm.M;
     return launch_status("pblock_forward_serial launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int pblock_forward_chunked(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out,
+                           int32_t n_chunks, void* const* ready_events, void* const* done_events, void* stream) {
+  try {
+    Dims dm;
+    int st = check_forward(h, x, w, cfg, out, &dm);
+    if (st != PBLOCK_OK) return st;
+    const pblock_cfg& c = *cfg;
+    if (n_chunks < 1 || n_chunks > c.S) return fail(PBLOCK_ERR_ARG, "n_chunks must be in [1, S]");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Ws ws = workspace(h);
+    const int64_t A = dm.A;
+    const int es = elem_size(c.dtype);
+    const char* xb = static_cast<const char*>(x);
+    char* ob = static_cast<char*>(out);
+    char* ub = static_cast<char*>(ws.u);
+    char* qb = static_cast<char*>(ws.qkv);
+    char* ab = static_cast<char*>(ws.ag);
+    for (int ck = 0; ck < n_chunks; ++ck) {
+      const int p0 = int(int64_t(ck) * c.S / n_chunks), p1 = int(int64_t(ck + 1) * c.S / n_chunks);
+      const int64_t rows = p1 - p0;
+      if (ready_events && ready_events[ck]) {
+        hipError_t e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(ready_events[ck]), 0);
+        if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipStreamWaitEvent: ") + hipGetErrorString(e));
+      }
+      for (int b = 0; b < c.B; ++b) {
+        const int64_t r0 = int64_t(b) * c.S + p0;
+        run_layernorm(xb + r0 * c.d * es, w->ln_gamma, w->ln_beta, ub + r0 * c.d * es, rows, c, s);
+      }
+      for (int b = 0; b < c.B; ++b) {
+        const int64_t r0 = int64_t(b) * c.S + p0;
+        run_gemm_in(ub + r0 * c.d * es, c.d, w->w_in, c.d, rows, dm.n_in, c.d, qb + r0 * 3 * A * es, 3 * A,
+                    ab + r0 * dm.k_out * es, dm.k_out, A, 3 * A, c.dtype, ws.scr, s);
+      }
+      // queries of this chunk; their keys reach back into earlier chunks, already projected
+      launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s, p0, p1);
+      for (int b = 0; b < c.B; ++b) {
+        const int64_t r0 = int64_t(b) * c.S + p0;
+        run_gemm_out(ab + r0 * dm.k_out * es, dm.k_out, w->w_out, dm.k_out, rows, c.d, dm.k_out, ob + r0 * c.d * es,
+                     c.add_residual ? xb + r0 * c.d * es : nullptr, c.dtype, ws.scr, s);
+      }
+      if (done_events && done_events[ck]) {
+        hipError_t e = hipEventRecord(static_cast<hipEvent_t>(done_events[ck]), s);
+        if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
+      }
+    }
+    h->last_m = dm.M;
+    return launch_status("pblock_forward_chunked launch");
   } catch (...) {
     return fail(PBLOCK_ERR_ARG, "internal error");
   }
