@@ -35,9 +35,10 @@
 // one workgroup each, in k-lockstep.  The remaining T mod G tiles would fill
 // only part of a last wave, so each is cut into `split` k-chunks
 // (split = G / tail) that run together as one more wave.  A chunk stores its
-// fp32 partial tile; a second small kernel sums the chunks of each tail tile
-// in chunk order (bitwise deterministic, no atomics, no cross-workgroup
-// fences) and applies the epilogue.
+// fp32 partial tile (row-major, written through the same LDS staging as the
+// epilogue); a second small kernel sums the chunks of each tail tile in chunk
+// order with coalesced reads (bitwise deterministic, no atomics, no
+// cross-workgroup fences) and applies the epilogue.
 //
 // L2 locality: workgroup ids are remapped so each XCD (id mod 8) owns a
 // contiguous run of work units, and units are ordered in groups of 8 M-tiles
@@ -81,7 +82,7 @@ constexpr int kGemmHalf = 256 * kGemmBK;  // elements of one operand tile of a s
 
 // Work decomposition of one GEMM launch (grid = dp_units + tail * split).
 struct GemmSched {
-  float* partials;  // [tail * split][kGemmBM * kGemmBN] fp32 (chunk slot, then float4 index, then thread)
+  float* partials;  // [tail * split][kGemmBM][kGemmBN] fp32, row-major partial tile per (tail tile, chunk)
   int tiles_m, tiles_n;
   int KT;           // k slabs per tile
   int dp_units;     // tiles computed whole (a multiple of the resident workgroup count)
@@ -118,31 +119,6 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier that no memory access may be moved across (the waits are explicit).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Epilogue of 4 consecutive columns n .. n+3 of row m (tail-reduce path).
-template <int EPI>
-__device__ __forceinline__ void store_outputs(const GemmArgs& g, int m, int n, float v0, float v1, float v2, float v3) {
-  uint16_t* dst;
-  if constexpr (EPI == kEpiSplitGelu) {
-    if (n < g.nsplit) {
-      dst = g.out0 + int64_t(m) * g.ld0 + n;
-    } else {
-      v0 = gelu_erf(v0); v1 = gelu_erf(v1); v2 = gelu_erf(v2); v3 = gelu_erf(v3);
-      dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
-    }
-  } else {
-    if (g.resid != nullptr) {
-      const u32x2 xr = *reinterpret_cast<const u32x2*>(g.resid + int64_t(m) * g.ldr + n);
-      v0 += __uint_as_float(xr.x << 16); v1 += __uint_as_float(xr.x & 0xFFFF0000u);
-      v2 += __uint_as_float(xr.y << 16); v3 += __uint_as_float(xr.y & 0xFFFF0000u);
-    }
-    dst = g.out0 + int64_t(m) * g.ld0 + n;
-  }
-  u32x2 o;
-  o.x = pack_bf16x2(v0, v1);
-  o.y = pack_bf16x2(v2, v3);
-  *reinterpret_cast<u32x2*>(dst) = o;
-}
 
 // Epilogue of 8 consecutive columns n .. n+7 of row m, one 16-byte store.
 template <int EPI>
@@ -331,26 +307,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   if (n & 1) slab(kt, a0, b0, a1, b1);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no copy may still be writing this workgroup's LDS
 
-  if (tl >= 0) {
-    constexpr int TILE4 = BM * BN / 4;
-    f32x4* mine = reinterpret_cast<f32x4*>(sk.partials) + int64_t(tl * sk.split + chunk) * TILE4;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r4 = (i * FN + j) * 4 + q;
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          mine[r4 * NT + tid] = v;
-        }
-    return;
-  }
-
   // Epilogue through LDS, four rounds: in round i every wave stages its rows wm*128 + i*32 +
   // 0..31 as fp32 (stage pair i&1, the wm half in its own array, 16-byte chunks XOR-permuted
-  // by row), then all threads store 64 full rows with 16-byte writes.  Lane (lr, lg) of MFMA
-  // tile (i, j) holds row lr and columns j*32 + 8*(r/4) + 4*lg + r%4.
+  // by row), then all threads store 64 full rows: bf16 outputs with 16-byte writes, or, for a
+  // split-K chunk, its fp32 partial tile (row-major 256 x 256) with 32-byte writes.  Lane
+  // (lr, lg) of MFMA tile (i, j) holds row lr and columns j*32 + 8*(r/4) + 4*lg + r%4.
+  float* part = tl >= 0 ? sk.partials + int64_t(tl * sk.split + chunk) * (BM * BN) : nullptr;
   lds_barrier();  // every wave is past its last fragment read
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -372,44 +334,40 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       const int c0 = (tid & 31) * 2;
       const f32x4 lo = *reinterpret_cast<const f32x4*>(src + lrow * 256 + ((c0 ^ (lrow & 15)) << 2));
       const f32x4 hi = *reinterpret_cast<const f32x4*>(src + lrow * 256 + (((c0 + 1) ^ (lrow & 15)) << 2));
-      const int m = m0 + half * 128 + i * 32 + lrow;
-      const int nn = n0 + (tid & 31) * 8;
-      if (m < g.M && nn < g.N) store_chunk8<EPI>(g, m, nn, lo, hi);
+      const int ml = half * 128 + i * 32 + lrow, nl = (tid & 31) * 8;
+      if (part != nullptr) {
+        f32x4* dst = reinterpret_cast<f32x4*>(part + ml * BN + nl);
+        dst[0] = lo;
+        dst[1] = hi;
+      } else if (m0 + ml < g.M && n0 + nl < g.N) {
+        store_chunk8<EPI>(g, m0 + ml, n0 + nl, lo, hi);
+      }
     }
   }
 }
 
 // Sums the k-chunk partials of each tail tile in chunk order and applies the epilogue.
-// grid = tail * 2 workgroups of 128 threads; workgroup (tile, half) handles the main
-// kernel's threads [128*half, 128*half + 128) of that tile.
+// grid = tail * 32 workgroups of 256 threads; workgroup (tile, b) handles rows 8b .. 8b+7
+// of the tile, thread t row 8b + t/32 and columns 8*(t%32) .. +7: coalesced 32-byte
+// partial reads and 16-byte output writes.
 template <int EPI>
-__global__ __launch_bounds__(128) void gemm_bf16_tail_reduce_kernel(GemmArgs g, GemmSched sk) {
-  constexpr int BM = kGemmBM, BN = kGemmBN, NT = kGemmThreads;
-  constexpr int FM = 4, FN = 4;
-  const int tl = blockIdx.x >> 1;
-  const int tid = (blockIdx.x & 1) * 128 + threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lg = lane >> 5;
+__global__ __launch_bounds__(256) void gemm_bf16_tail_reduce_kernel(GemmArgs g, GemmSched sk) {
+  constexpr int BM = kGemmBM, BN = kGemmBN;
+  const int tl = blockIdx.x >> 5;
+  const int r = (blockIdx.x & 31) * 8 + (threadIdx.x >> 5);
+  const int c = (threadIdx.x & 31) * 8;
   int tm, tn;
   tile_coords(sk.dp_units + tl, sk.tiles_m, sk.tiles_n, &tm, &tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  constexpr int TILE4 = BM * BN / 4;
-  const f32x4* base = reinterpret_cast<const f32x4*>(sk.partials) + int64_t(tl * sk.split) * TILE4;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * 128 + i * 32 + lr;
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r4 = (i * FN + j) * 4 + q;
-        f32x4 s = base[r4 * NT + tid];
-        for (int c = 1; c < sk.split; ++c) s += base[int64_t(c) * TILE4 + r4 * NT + tid];
-        const int n = n0 + wn * 128 + j * 32 + q * 8 + lg * 4;
-        if (m < g.M && n < g.N) store_outputs<EPI>(g, m, n, s[0], s[1], s[2], s[3]);
-      }
+  const int m = tm * BM + r, n = tn * BN + c;
+  if (m >= g.M || n >= g.N) return;
+  const f32x4* src = reinterpret_cast<const f32x4*>(sk.partials + int64_t(tl * sk.split) * (BM * BN) + r * BN + c);
+  f32x4 lo = src[0], hi = src[1];
+  for (int k = 1; k < sk.split; ++k) {
+    src += (BM * BN) / 4;
+    lo += src[0];
+    hi += src[1];
   }
+  store_chunk8<EPI>(g, m, n, lo, hi);
 }
 
 }  // namespace pblk

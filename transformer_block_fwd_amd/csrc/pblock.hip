@@ -221,7 +221,7 @@ void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s) {
   const unsigned grid = unsigned(p.dp_units + p.tail * p.split);
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
   if (p.tail > 0)
-    hipLaunchKernelGGL((gemm_bf16_tail_reduce_kernel<EPI>), dim3(unsigned(p.tail * 2)), dim3(128), 0, s, g, sk);
+    hipLaunchKernelGGL((gemm_bf16_tail_reduce_kernel<EPI>), dim3(unsigned(p.tail * 32)), dim3(256), 0, s, g, sk);
 }
 
 template <int EPI>
