@@ -302,6 +302,19 @@ def main():
                 "tflops": round(cfg.flops() / (med * 1e-3) / 1e12, 3)}
         print(f"[bench] cold-cache median {med:.3f} ms", file=sys.stderr, flush=True)
 
+    # a plain device copy of x's bytes (read M*d, write M*d), back to back so x stays in the
+    # last-level cache: an upper bound for LayerNorm, which inside the step reads x after the
+    # GEMMs have streamed the weights through that cache
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        out.copy_(dev["x"])
+    c0.record(stream)
+    for _ in range(20):
+        out.copy_(dev["x"])
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * dev["x"].numel() * dev["x"].element_size() / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9
+
     mfma_tflops = mfma_loop_rate(tb, torch, stream)
     print(f"[bench] register-only MFMA loop {mfma_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
@@ -329,6 +342,7 @@ def main():
             es = 2 if cfg.dtype == "bf16" else 4
             n_ln = 2 if args.block == "serial" else 1
             rec["gbs"] = round(n_ln * (2 * cfg.M * cfg.d * es + 2 * cfg.d * es) / (ms * 1e-3) / 1e9, 1)
+            rec["plain_copy_warm_gbs"] = round(copy_gbs, 1)
         per_kernel[k] = rec
 
     result = {

@@ -177,13 +177,24 @@ template <typename T>
 void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d, float eps, hipStream_t s) {
   const int per = 16 / int(sizeof(T));
   const int need = (d / per + kLnThreads - 1) / kLnThreads;
-  const dim3 grid{static_cast<unsigned>(M)}, block{kLnThreads};
-  if (need <= 1) hipLaunchKernelGGL((layernorm_kernel<T, 1>), grid, block, 0, s, x, g, b, u, d, eps);
-  else if (need <= 2) hipLaunchKernelGGL((layernorm_kernel<T, 2>), grid, block, 0, s, x, g, b, u, d, eps);
-  else if (need <= 4) hipLaunchKernelGGL((layernorm_kernel<T, 4>), grid, block, 0, s, x, g, b, u, d, eps);
-  else if (need <= 8) hipLaunchKernelGGL((layernorm_kernel<T, 8>), grid, block, 0, s, x, g, b, u, d, eps);
-  else if (need <= 16) hipLaunchKernelGGL((layernorm_kernel<T, 16>), grid, block, 0, s, x, g, b, u, d, eps);
-  else hipLaunchKernelGGL((layernorm_kernel<T, 32>), grid, block, 0, s, x, g, b, u, d, eps);
+  // Rows per workgroup: wide rows (>= 16 KiB) gain from gamma/beta reuse and the next-row
+  // prefetch, narrow ones from more workgroups; at least 512 workgroups either way.  Rows
+  // wider than 8 vectors per thread go one per workgroup.
+  const int64_t row_bytes = int64_t(d) * int64_t(sizeof(T));
+  const int want = row_bytes >= 16384 ? kLnMaxRows : (row_bytes >= 4096 ? 2 : 1);
+  const int rows = need > 8 ? 1 : int(std::max<int64_t>(1, std::min<int64_t>(want, M / 512)));
+  const dim3 grid{static_cast<unsigned>((M + rows - 1) / rows)}, block{kLnThreads};
+#define PBLK_LN(V) hipLaunchKernelGGL((layernorm_kernel<T, V>), grid, block, 0, s, x, g, b, u, M, d, rows, eps)
+  if (need <= 1) PBLK_LN(1);
+  else if (need <= 2) PBLK_LN(2);
+  else if (need <= 3) PBLK_LN(3);
+  else if (need <= 4) PBLK_LN(4);
+  else if (need <= 6) PBLK_LN(6);
+  else if (need <= 8) PBLK_LN(8);
+  else if (need <= 12) PBLK_LN(12);
+  else if (need <= 16) PBLK_LN(16);
+  else PBLK_LN(32);
+#undef PBLK_LN
 }
 
 // GEMM scratch: fp32 partial tiles of the split-K tail (at most one wave of chunks).
