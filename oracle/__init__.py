@@ -6,9 +6,13 @@ benchmark's CPU-baseline leg, never by the library.
 from .block import (  # noqa: F401
     block_forward,
     block_forward_rows,
+    block_forward_variant,
+    block_forward_variant_rows,
     gelu,
+    gelu_tanh,
     layer_norm,
     relative_error,
+    rope,
     serial_block_forward,
     serial_block_forward_rows,
     split_projection,

@@ -34,14 +34,20 @@ grows with S*W rather than S^2.
 
 The serial (pre-LayerNorm) layer the parallel block replaces is here too, for
 the comparison of the two forms (section 2 contrasts them; section 8's ablation
-prices the parallel form); "standard layer" is read as the pre-LN layout.
+prices the parallel form); "standard layer" is read as the pre-LN layout.  So
+are the alternatives to the silent choices above, as explicit switches of
+block_forward_variant: the tanh GeLU, linear biases, rotary position embedding
+of q and k (RoFormer), and a second LayerNorm for the MLP branch.
 
 Pins (all in the CPU test-suite): dense brute-force band attention, W >= S vs
 torch's causal attention, W = 1 closed form, 2-key closed form, the branch-sum
 identity, LayerNorm and GeLU against torch and math.erf, tensor-parallel
 decomposition, locality, and hand-derived closed-form blocks; the serial layer
 against torch library routines and, with one sub-layer switched off, against
-the parallel block.
+the parallel block; the variant switches against torch library routines
+(layer_norm, linear with bias, tanh gelu) with the rotation done as complex
+multiplication, RoPE's dependence on relative position only, hand-computed
+rotations, and reduction to block_forward with every switch off.
 """
 from __future__ import annotations
 
@@ -227,6 +233,115 @@ def serial_block_forward_rows(x, gamma, beta, gamma2, beta2, w_in, w_out, H: int
         h = xs[i0 - j0:] + o.reshape(-1, A) @ w_out[:, :A].T
         u2 = layer_norm(h, gamma2, beta2, eps)
         outs.append(h + gelu(u2 @ w_in[3 * A:].T) @ w_out[:, A:].T)
+    return outs
+
+
+# ----------------------------------------------------------------------------- variant knobs
+# The pages leave several choices open (no positional encoding, bias or GeLU form is named,
+# and "the same input" could be one LayerNorm or one per branch).  The functions below add
+# each alternative as an explicit switch; with every switch off they reduce to
+# block_forward.
+
+
+def gelu_tanh(z):
+    """GeLU's tanh approximation (Hendrycks and Gimpel, "Gaussian Error Linear Units",
+    section 2): z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3)))."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def rope(t, positions, base: float):
+    """Rotary position embedding (RoFormer, Su et al., section 3): in every head vector of
+    hd features, the pair (t[2i], t[2i+1]) at position p is rotated by the angle
+    p * base^(-2i/hd), i = 0 .. hd/2 - 1.
+
+    t: [n, H, hd] for the positions in ``positions`` (length n).  Returns a new array.
+    """
+    t = np.asarray(t, np.float64)
+    hd = t.shape[-1]
+    theta = float(base) ** (-2.0 * np.arange(hd // 2) / hd)  # [hd/2]
+    ang = np.asarray(positions, np.float64)[:, None] * theta[None, :]  # [n, hd/2]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    even, odd = t[..., 0::2], t[..., 1::2]
+    out = np.empty_like(t)
+    out[..., 0::2] = even * c - odd * s
+    out[..., 1::2] = even * s + odd * c
+    return out
+
+
+def _variant_rows(xs, pos0, q_from, gamma, beta, w_in, w_out, H, hd, W, eps, add_residual, gelu_form, b_in,
+                  b_out, rope_base, gamma2, beta2):
+    """Output rows q_from.. of one sequence slice xs (positions pos0 .. pos0+len-1), whose
+    first rows supply the keys the later queries reach."""
+    A = H * hd
+    u_attn = layer_norm(xs, gamma, beta, eps)
+    u_mlp = u_attn if gamma2 is None else layer_norm(xs, gamma2, beta2, eps)
+    z = u_attn @ w_in[:3 * A].T
+    f = u_mlp[q_from:] @ w_in[3 * A:].T
+    if b_in is not None:
+        z = z + b_in[:3 * A]
+        f = f + b_in[3 * A:]
+    q, k, v, _ = split_projection(z, H, hd)
+    if rope_base is not None:
+        pos = pos0 + np.arange(xs.shape[0])
+        q = rope(q, pos, rope_base)
+        k = rope(k, pos, rope_base)
+    o = swa_attention(q[q_from:], k, v, W, q_pos0=pos0 + q_from, k_pos0=pos0)
+    act = gelu(f) if gelu_form == "erf" else gelu_tanh(f)
+    y = np.concatenate([o.reshape(-1, A), act], axis=-1) @ w_out.T
+    if b_out is not None:
+        y = y + b_out
+    if add_residual:
+        y = y + xs[q_from:]
+    return y
+
+
+def _check_gelu_form(gelu_form):
+    if gelu_form not in ("erf", "tanh"):
+        raise ValueError("gelu_form must be 'erf' or 'tanh'")
+
+
+def block_forward_variant(x, gamma, beta, w_in, w_out, H: int, hd: int, W: int, eps: float = 1e-5,
+                          add_residual: bool = True, gelu_form: str = "erf", b_in=None, b_out=None,
+                          rope_base=None, gamma2=None, beta2=None):
+    """The parallel block with the open choices as switches:
+
+        ua = LN(x; gamma, beta);  um = ua, or LN(x; gamma2, beta2) with a second LayerNorm
+        [q | k | v] = ua W_qkv^T (+ b_in[:3A]);  f = um W_1^T (+ b_in[3A:])
+        q, k rotated by their position (rope_base given), positions 0 .. S-1 per sequence
+        y = [Attn_SWA(q, k, v) | act(f)] W_out^T (+ b_out) (+ x),  act = exact or tanh GeLU.
+    """
+    _check_gelu_form(gelu_form)
+    x = np.asarray(x, np.float64)
+    w_in = np.asarray(w_in, np.float64)
+    w_out = np.asarray(w_out, np.float64)
+    b_in = None if b_in is None else np.asarray(b_in, np.float64)
+    b_out = None if b_out is None else np.asarray(b_out, np.float64)
+    B, S, d = x.shape
+    y = np.empty((B, S, d))
+    for b in range(B):
+        y[b] = _variant_rows(x[b], 0, 0, gamma, beta, w_in, w_out, H, hd, W, eps, add_residual, gelu_form, b_in,
+                             b_out, rope_base, gamma2, beta2)
+    return y
+
+
+def block_forward_variant_rows(x, gamma, beta, w_in, w_out, H: int, hd: int, W: int, row_blocks,
+                               eps: float = 1e-5, add_residual: bool = True, gelu_form: str = "erf", b_in=None,
+                               b_out=None, rope_base=None, gamma2=None, beta2=None):
+    """Output rows y[b, i0:i1] of block_forward_variant for each (b, i0, i1) in
+    ``row_blocks``, forming only the keys those queries reach (positions i0-W+1 ..)."""
+    _check_gelu_form(gelu_form)
+    w_in = np.asarray(w_in, np.float64)
+    w_out = np.asarray(w_out, np.float64)
+    b_in = None if b_in is None else np.asarray(b_in, np.float64)
+    b_out = None if b_out is None else np.asarray(b_out, np.float64)
+    outs = []
+    for b, i0, i1 in row_blocks:
+        j0 = window_lo(i0, W)
+        xs = np.asarray(x[b, j0:i1], np.float64)
+        outs.append(_variant_rows(xs, j0, i0 - j0, gamma, beta, w_in, w_out, H, hd, W, eps, add_residual,
+                                  gelu_form, b_in, b_out, rope_base, gamma2, beta2))
     return outs
 
 

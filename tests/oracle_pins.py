@@ -11,7 +11,11 @@ reference values come from, in turn:
     is a logistic function), uniform attention when Q is zero, LayerNorm of
     zero-mean unit-variance sign patterns, the normal CDF at 1;
   * invariants: branch-sum identity, tensor-parallel decomposition, locality of
-    the window, batch independence.
+    the window, batch independence;
+  * for the variant switches: torch's linear-with-bias and tanh gelu, the rotary
+    embedding as complex multiplication (RoFormer's complex form), rotations of
+    basis vectors worked out by hand, and RoPE's dependence on relative position
+    only.
 """
 from __future__ import annotations
 
@@ -89,6 +93,54 @@ def _torch_serial_block(x, g1, b1, g2, b2, w_in, w_out, H, hd, W, eps):
     h = tx + F.linear(o, wo[:, :A])
     u2 = F.layer_norm(h, (d,), torch.from_numpy(g2), torch.from_numpy(b2), eps)
     return (h + F.linear(F.gelu(F.linear(u2, wi[3 * A:]), approximate="none"), wo[:, A:])).numpy()
+
+
+def _torch_rope(t, base):
+    """[B, S, H, hd] -> rotated, as RoFormer's complex form: the pair (t_2i, t_2i+1) is the
+    complex number t_2i + i t_2i+1, multiplied by e^(i p theta_i), theta_i = base^(-2i/hd)."""
+    B, S, H, hd = t.shape
+    theta = torch.pow(torch.tensor(float(base), dtype=torch.float64), -torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+    ang = torch.arange(S, dtype=torch.float64)[:, None] * theta[None, :]
+    rot = torch.polar(torch.ones_like(ang), ang)  # [S, hd/2]
+    tc = torch.view_as_complex(t.reshape(B, S, H, hd // 2, 2).contiguous())
+    return torch.view_as_real(tc * rot[None, :, None, :]).reshape(B, S, H, hd)
+
+
+def _torch_variant_block(x, g, b, wi, wo, H, hd, W, eps, add_residual=True, gelu_form="erf", b_in=None, b_out=None,
+                         rope_base=None, g2=None, b2=None):
+    """The variant block from torch float64 library routines (layer_norm, linear with bias,
+    gelu in either form, band-masked scaled-dot-product attention), RoPE as complex products."""
+    tx = torch.from_numpy(x)
+    B, S, d = x.shape
+    A = H * hd
+    t = torch.from_numpy
+    ua = F.layer_norm(tx, (d,), t(g), t(b), eps)
+    um = ua if g2 is None else F.layer_norm(tx, (d,), t(g2), t(b2), eps)
+    wi_t = t(wi)
+    bi = None if b_in is None else t(b_in)
+    z = F.linear(ua, wi_t[:3 * A], None if bi is None else bi[:3 * A])
+    f = F.linear(um, wi_t[3 * A:], None if bi is None else bi[3 * A:])
+    q, k, v = (z[..., c * A:(c + 1) * A].reshape(B, S, H, hd) for c in range(3))
+    if rope_base is not None:
+        q, k = _torch_rope(q, rope_base), _torch_rope(k, rope_base)
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    o = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2),
+                                       attn_mask=(j <= i) & (j > i - W)).transpose(1, 2).reshape(B, S, A)
+    act = F.gelu(f, approximate="none" if gelu_form == "erf" else "tanh")
+    y = F.linear(torch.cat([o, act], dim=-1), t(wo), None if b_out is None else t(b_out))
+    if add_residual:
+        y = y + tx
+    return y.numpy()
+
+
+def _variant_params(seed, d, n_in, two_ln=True):
+    rng = _rng(seed)
+    b_in = 0.3 * rng.standard_normal(n_in)
+    b_out = 0.3 * rng.standard_normal(d)
+    g2 = 1.0 + 0.3 * rng.standard_normal(d) if two_ln else None
+    b2 = 0.2 * rng.standard_normal(d) if two_ln else None
+    return b_in, b_out, g2, b2
 
 
 # ----------------------------------------------------------------------------- attention
@@ -382,6 +434,116 @@ def pin_serial_rows_match_full(ob):
         np.testing.assert_allclose(y, full[b, i0:i1], rtol=1e-12, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------- variant switches
+
+
+def pin_gelu_tanh(ob):
+    """tanh GeLU == torch's tanh-approximate gelu and a math.tanh loop; it stays within
+    1e-3 of the exact form and differs from it by more than 1e-4 somewhere."""
+    z = np.linspace(-9, 9, 2001)
+    got = ob.gelu_tanh(z)
+    np.testing.assert_allclose(got, F.gelu(torch.from_numpy(z), approximate="tanh").numpy(), rtol=1e-13,
+                               atol=1e-15)
+    loop = np.array([0.5 * t * (1 + math.tanh(math.sqrt(2 / math.pi) * (t + 0.044715 * t ** 3))) for t in z])
+    np.testing.assert_allclose(got, loop, rtol=1e-13, atol=1e-15)
+    gap = np.abs(got - ob.gelu(z)).max()
+    assert 1e-4 < gap < 1e-3, gap
+
+
+def pin_rope_hand_values(ob):
+    """Rotations of basis vectors worked out by hand: hd = 4, base 10000, so the two pair
+    frequencies are 1 and 10000^(-1/2) = 0.01; e0 at position p goes to (cos p, sin p, 0, 0),
+    e3 to (0, 0, -sin 0.01p, cos 0.01p); position 0 is the identity."""
+    pos = np.array([0, 1, 3, 1000])
+    for p_idx, p in enumerate(pos):
+        e0 = np.zeros((len(pos), 1, 4))
+        e0[:, 0, 0] = 1.0
+        e3 = np.zeros((len(pos), 1, 4))
+        e3[:, 0, 3] = 1.0
+        r0 = ob.rope(e0, pos, 10000.0)[p_idx, 0]
+        r3 = ob.rope(e3, pos, 10000.0)[p_idx, 0]
+        np.testing.assert_allclose(r0, [math.cos(p), math.sin(p), 0, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r3, [0, 0, -math.sin(0.01 * p), math.cos(0.01 * p)], rtol=0, atol=1e-12)
+
+
+def pin_rope_relative_position(ob):
+    """RoPE scores depend on relative position only: q at p and k at p' score the same as
+    at p + c and p' + c; it is a rotation (norms kept); and a block whose windows never
+    reach a prepended prefix gives the same rows as without the prefix."""
+    rng = _rng(91)
+    q = rng.standard_normal((1, 3, 16))
+    k = rng.standard_normal((1, 3, 16))
+    for p, pp in ((5, 2), (40, 40), (7, 100)):
+        base = np.einsum("hd,hd->h", ob.rope(q, [p], 500.0)[0], ob.rope(k, [pp], 500.0)[0])
+        for c in (1, 13, 999):
+            sh = np.einsum("hd,hd->h", ob.rope(q, [p + c], 500.0)[0], ob.rope(k, [pp + c], 500.0)[0])
+            np.testing.assert_allclose(sh, base, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(ob.rope(q, [17], 500.0), axis=-1), np.linalg.norm(q, axis=-1),
+                               rtol=1e-13)
+    B, S, d, H, hd, ffn, W, P = 1, 30, 16, 2, 8, 24, 5, 11
+    x, g, b, wi, wo = _rand_block(92, B, S + P, d, H, hd, ffn)
+    long = ob.block_forward_variant(x, g, b, wi, wo, H, hd, W, rope_base=100.0)
+    short = ob.block_forward_variant(x[:, P:], g, b, wi, wo, H, hd, W, rope_base=100.0)
+    np.testing.assert_allclose(long[:, P + W - 1:], short[:, W - 1:], rtol=1e-11, atol=1e-12)
+    assert np.abs(long[:, P:P + W - 1] - short[:, :W - 1]).max() > 1e-6
+
+
+def pin_variant_vs_torch(ob):
+    """Each switch alone and all together == the torch-assembled block (odd shapes, several W)."""
+    cases = [
+        (101, (2, 45, 24, 3, 8, 40), 9, dict(gelu_form="tanh")),
+        (102, (1, 70, 32, 2, 16, 48), 70, dict(bias=True)),
+        (103, (2, 33, 16, 2, 8, 24), 6, dict(rope_base=10000.0)),
+        (104, (1, 50, 24, 1, 16, 40), 17, dict(two_ln=True)),
+        (105, (3, 21, 16, 2, 8, 16), 4, dict(gelu_form="tanh", bias=True, rope_base=50.0, two_ln=True)),
+    ]
+    for seed, (B, S, d, H, hd, ffn), W, kw in cases:
+        x, g, b, wi, wo = _rand_block(seed, B, S, d, H, hd, ffn)
+        b_in, b_out, g2, b2 = _variant_params(seed + 1, d, wi.shape[0])
+        args = dict(gelu_form=kw.get("gelu_form", "erf"), rope_base=kw.get("rope_base"))
+        if kw.get("bias"):
+            args.update(b_in=b_in, b_out=b_out)
+        for add_res in (True, False):
+            got = ob.block_forward_variant(x, g, b, wi, wo, H, hd, W, add_residual=add_res, **args,
+                                           gamma2=g2 if kw.get("two_ln") else None,
+                                           beta2=b2 if kw.get("two_ln") else None)
+            ref = _torch_variant_block(x, g, b, wi, wo, H, hd, W, 1e-5, add_res, **args,
+                                       g2=g2 if kw.get("two_ln") else None, b2=b2 if kw.get("two_ln") else None)
+            np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+
+
+def pin_variant_reductions(ob):
+    """With every switch off the variant block is block_forward; the second LayerNorm with
+    the first one's parameters changes nothing; at W = 1 RoPE changes nothing (a token
+    attending only to itself gets its own v, which is not rotated), and the attention branch
+    is (u W_v^T + b_v) W_o^T."""
+    B, S, d, H, hd, ffn, W = 2, 27, 16, 2, 8, 24, 7
+    x, g, b, wi, wo = _rand_block(111, B, S, d, H, hd, ffn)
+    b_in, b_out, _, _ = _variant_params(112, d, wi.shape[0], two_ln=False)
+    np.testing.assert_allclose(ob.block_forward_variant(x, g, b, wi, wo, H, hd, W),
+                               ob.block_forward(x, g, b, wi, wo, H, hd, W), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(ob.block_forward_variant(x, g, b, wi, wo, H, hd, W, gamma2=g, beta2=b),
+                               ob.block_forward(x, g, b, wi, wo, H, hd, W), rtol=1e-13, atol=1e-14)
+    A = H * hd
+    r1 = ob.block_forward_variant(x, g, b, wi, wo, H, hd, 1, b_in=b_in, b_out=b_out, rope_base=10.0)
+    u = F.layer_norm(torch.from_numpy(x), (d,), torch.from_numpy(g), torch.from_numpy(b), 1e-5).numpy()
+    ref = x + (u @ wi[2 * A:3 * A].T + b_in[2 * A:3 * A]) @ wo[:, :A].T \
+        + F.gelu(torch.from_numpy(u @ wi[3 * A:].T + b_in[3 * A:])).numpy() @ wo[:, A:].T + b_out
+    np.testing.assert_allclose(r1, ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_variant_rows_match_full(ob):
+    """block_forward_variant_rows == slices of block_forward_variant, every switch on."""
+    B, S, d, H, hd, ffn, W = 2, 90, 16, 2, 8, 24, 13
+    x, g, b, wi, wo = _rand_block(121, B, S, d, H, hd, ffn)
+    b_in, b_out, g2, b2 = _variant_params(122, d, wi.shape[0])
+    kw = dict(gelu_form="tanh", b_in=b_in, b_out=b_out, rope_base=1000.0, gamma2=g2, beta2=b2)
+    full = ob.block_forward_variant(x, g, b, wi, wo, H, hd, W, **kw)
+    blocks = [(0, 0, 7), (1, 5, 30), (1, 60, 90), (0, 12, 13)]
+    for (bb, i0, i1), y in zip(blocks, ob.block_forward_variant_rows(x, g, b, wi, wo, H, hd, W, blocks, **kw)):
+        np.testing.assert_allclose(y, full[bb, i0:i1], rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [
     pin_attention_brute_force,
     pin_attention_vs_torch_band,
@@ -401,4 +563,10 @@ ALL_PINS = [
     pin_serial_vs_torch,
     pin_serial_single_sublayer,
     pin_serial_rows_match_full,
+    pin_gelu_tanh,
+    pin_rope_hand_values,
+    pin_rope_relative_position,
+    pin_variant_vs_torch,
+    pin_variant_reductions,
+    pin_variant_rows_match_full,
 ]

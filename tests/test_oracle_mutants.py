@@ -44,6 +44,19 @@ MUTANTS = {
     "serial_no_inner_residual": [("h = x + o.reshape(B, S, A) @ w_out[:, :A].T", "h = o.reshape(B, S, A) @ w_out[:, :A].T")],
     "serial_mlp_residual_from_x": [("    return h + gelu(u2 @ w_in[3 * A:].T) @ w_out[:, A:].T",
                                     "    return x + gelu(u2 @ w_in[3 * A:].T) @ w_out[:, A:].T")],
+    "gelu_tanh_wrong_cubic": [("0.044715 * z ** 3", "0.04715 * z ** 3")],
+    "gelu_form_ignored": [('act = gelu(f) if gelu_form == "erf" else gelu_tanh(f)', "act = gelu(f)")],
+    "rope_half_split_pairs": [("even, odd = t[..., 0::2], t[..., 1::2]", "even, odd = t[..., :hd // 2], t[..., hd // 2:]"),
+                              ("out[..., 0::2] = even * c - odd * s", "out[..., :hd // 2] = even * c - odd * s"),
+                              ("out[..., 1::2] = even * s + odd * c", "out[..., hd // 2:] = even * s + odd * c")],
+    "rope_rotates_backwards": [("out[..., 0::2] = even * c - odd * s", "out[..., 0::2] = even * c + odd * s"),
+                               ("out[..., 1::2] = even * s + odd * c", "out[..., 1::2] = -even * s + odd * c")],
+    "rope_frequency_exponent": [("(-2.0 * np.arange(hd // 2) / hd)", "(-1.0 * np.arange(hd // 2) / hd)")],
+    "rope_on_v_too": [("        k = rope(k, pos, rope_base)\n", "        k = rope(k, pos, rope_base)\n        v = rope(v, pos, rope_base)\n")],
+    "rope_only_q": [("        k = rope(k, pos, rope_base)\n", "")],
+    "bias_in_skips_mlp": [("f = f + b_in[3 * A:]", "f = f")],
+    "bias_out_dropped": [("y = y + b_out", "y = y")],
+    "two_ln_swapped": [("z = u_attn @ w_in[:3 * A].T", "z = u_mlp @ w_in[:3 * A].T")],
 }
 
 
