@@ -15,6 +15,7 @@ run, and the fp64 CPU oracle timed on the host as a baseline.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload shard175b]
                   [--block parallel|serial] [--window W] [--chunks N]
+                  [--gelu-tanh] [--bias] [--rope BASE] [--two-ln]   # variant switches
   python bench.py --sweep      # attention time against window and sequence length
 """
 from __future__ import annotations
@@ -62,6 +63,11 @@ def parse():
     p.add_argument("--chunks", type=int, default=0,
                    help="time the forward in this many position chunks (the TP/SP overlap form) with a completion "
                         "event per chunk; per-kernel and roofline figures then come from an unchunked pass")
+    p.add_argument("--gelu-tanh", action="store_true", help="variant: tanh-form GeLU")
+    p.add_argument("--bias", action="store_true", help="variant: biases on both projections")
+    p.add_argument("--rope", type=float, default=0.0, metavar="BASE",
+                   help="variant: rotary embedding of q and k with this base (0: off)")
+    p.add_argument("--two-ln", action="store_true", help="variant: a second LayerNorm for the MLP branch")
     p.add_argument("--cold-steps", type=int, default=10, help="cold-cache steps after the timed run (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -83,7 +89,7 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
 
 
-def cpu_baseline(cfg, inp, block, ln2) -> dict:
+def cpu_baseline(cfg, inp, block, ln2, variant=None) -> dict:
     """The fp64 oracle, as it stands, timed once on the host cores over the whole workload."""
     import oracle
 
@@ -97,6 +103,9 @@ def cpu_baseline(cfg, inp, block, ln2) -> dict:
     if block == "serial":
         oracle.serial_block_forward(inp.x, inp.gamma, inp.beta, ln2["gamma2"], ln2["beta2"], inp.w_in, inp.w_out,
                                     cfg.H, cfg.hd, cfg.W, eps=cfg.ln_eps)
+    elif variant is not None:
+        oracle.block_forward_variant(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W,
+                                     eps=cfg.ln_eps, add_residual=bool(cfg.add_residual), **variant)
     else:
         oracle.block_forward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W, eps=cfg.ln_eps,
                              add_residual=bool(cfg.add_residual))
@@ -197,7 +206,7 @@ def main():
     import torch
 
     import transformer_block_fwd_amd as tb
-    from workload import CONFIGS, make_inputs, make_ln2
+    from workload import CONFIGS, make_inputs, make_ln2, make_variant_params
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -218,6 +227,12 @@ def main():
     arrs = inp.device_arrays()
     ln2 = make_ln2(cfg, seed=0)
     arrs["gamma2"], arrs["beta2"] = ln2["gamma2_dev"], ln2["beta2_dev"]
+    use_variant = bool(args.gelu_tanh or args.bias or args.rope or args.two_ln)
+    if use_variant and args.block != "parallel":
+        raise SystemExit("the variant switches apply to the parallel block")
+    vp = make_variant_params(cfg, seed=0)
+    if args.bias:
+        arrs["b_in"], arrs["b_out"] = vp["b_in_dev"], vp["b_out_dev"]
     if cfg.dtype == "bf16":
         dev = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).cuda()
                for k, v in arrs.items()}
@@ -228,13 +243,30 @@ def main():
     stream = torch.cuda.current_stream()
     h = tb.pblock_create(cfg)
 
-    if args.chunks and args.block != "parallel":
-        raise SystemExit("--chunks applies to the parallel block")
+    if args.chunks and (args.block != "parallel" or use_variant):
+        raise SystemExit("--chunks applies to the parallel block without variant switches")
+    variant = tb.make_variant(gelu_tanh=args.gelu_tanh, rope=bool(args.rope), rope_base=args.rope or 10000.0,
+                              two_ln=args.two_ln)
+    extra = {k: dev[k] for k in ("b_in", "b_out") if k in dev}
+    if args.two_ln:
+        extra.update(ln2_gamma=dev["gamma2"], ln2_beta=dev["beta2"])
+    variant_desc = None
+    oracle_variant = None
+    if use_variant:
+        variant_desc = {"gelu": "tanh" if args.gelu_tanh else "erf", "bias": bool(args.bias),
+                        "rope_base": args.rope or None, "two_ln": bool(args.two_ln)}
+        oracle_variant = dict(gelu_form=variant_desc["gelu"], rope_base=variant_desc["rope_base"])
+        if args.bias:
+            oracle_variant.update(b_in=vp["b_in"], b_out=vp["b_out"])
+        if args.two_ln:
+            oracle_variant.update(gamma2=ln2["gamma2"], beta2=ln2["beta2"])
     done = [torch.cuda.Event(enable_timing=True) for _ in range(args.chunks)]
 
     def step(chunked=bool(args.chunks)):
         if args.block == "serial":
             tb.pblock_forward_serial(h, dev["x"], weights, (dev["gamma2"], dev["beta2"]), cfg, out, stream)
+        elif use_variant:
+            tb.pblock_forward_variant(h, dev["x"], weights, extra, cfg, variant, out, stream)
         elif chunked:
             tb.pblock_forward_chunked(h, dev["x"], weights, cfg, out, args.chunks, None, done, stream)
         else:
@@ -324,13 +356,14 @@ def main():
     k_avg = {k: v / max(n_fwd, 1) for k, v in kernel_ms.items()}
     g1_ms = k_avg["gemm_in"]
     g1_flops = cfg.gemm1_flops()
-    as_profiled = args.block == "parallel" and not args.window and args.add_residual is None and not args.chunks
+    as_profiled = (args.block == "parallel" and not args.window and args.add_residual is None and not args.chunks
+                   and not use_variant)
     traffic = MEASURED_TRAFFIC_BYTES.get(cfg.name) if as_profiled else None
     roofline = {"kernel": "gemm_in (fused QKV+FC1 GEMM, GeLU epilogue)", "bound": "mfma",
                 "achieved": round(g1_flops / (g1_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(g1_flops / (g1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_flops_per_launch": g1_flops, "avg_launch_ms": round(g1_ms, 5)}
-    if args.block == "serial":
+    if args.block == "serial" or args.two_ln:
         roofline["kernel"] = "gemm_in (QKV GEMM + FC1 GEMM with GeLU epilogue, summed per forward)"
     per_kernel = {}
     for k, ms in k_avg.items():
@@ -340,7 +373,7 @@ def main():
             rec["tflops"] = round(kf / (ms * 1e-3) / 1e12, 2)
         if k == "layernorm":
             es = 2 if cfg.dtype == "bf16" else 4
-            n_ln = 2 if args.block == "serial" else 1
+            n_ln = 2 if (args.block == "serial" or args.two_ln) else 1
             rec["gbs"] = round(n_ln * (2 * cfg.M * cfg.d * es + 2 * cfg.d * es) / (ms * 1e-3) / 1e9, 1)
             rec["plain_copy_warm_gbs"] = round(copy_gbs, 1)
         per_kernel[k] = rec
@@ -360,7 +393,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
         "config": {"workload": f"{cfg.name}: {WORKLOAD_NOTES.get(cfg.name, '')}", "block": args.block, "B": cfg.B,
                    "S": cfg.S, "d": cfg.d, "H": cfg.H, "hd": cfg.hd, "ffn": cfg.ffn, "W": cfg.W,
-                   "add_residual": cfg.add_residual, "parallelism": "single GPU"},
+                   "add_residual": cfg.add_residual, "parallelism": "single GPU", "variant": variant_desc},
         "pct_peak_bf16": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.M / (ms_step * 1e-3), 1),
         "algorithmic_gflop_per_step": round(flops / 1e9, 3),
@@ -378,7 +411,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.block, ln2)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.block, ln2, oracle_variant)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -93,9 +93,10 @@ int pblock_validate_cfg(const pblock_cfg* cfg);
  * Host only.  The workspace holds the intermediates u [Mt, d], QKV [M, 3*H*hd],
  * AG [Mt, H*hd + ffn] (M = B*S; the GEMM row operands u and AG get M rounded
  * up to 256 plus 256 more rows, Mt, since the GEMM reads its row operand to
- * the end of a 256-row tile from any starting row) and, for bf16, the GEMM
- * scratch for the split-K tail wave: one fp32 256x256 partial tile per
- * compute unit (this estimate assumes 256). */
+ * the end of a 256-row tile from any starting row), for bf16 the GEMM
+ * scratch for the split-K tail wave (one fp32 256x256 partial tile per
+ * compute unit; this estimate assumes 256), and the rotary-embedding table of
+ * pblock_forward_variant (fp32 cos and sin for hd/2 pairs at M positions). */
 int64_t pblock_workspace_bytes(const pblock_cfg* cfg);
 
 /* Algorithmic FLOPs of one forward for cfg: 2*M*d*(3*H*hd+ffn) +
@@ -156,6 +157,57 @@ int pblock_forward_serial(pblock_t h, const void* x, const pblock_weights* w, co
 int pblock_forward_chunked(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg,
                            void* out, int32_t n_chunks, void* const* ready_events, void* const* done_events,
                            void* stream);
+
+/* Switches for the choices the pages leave open (MegaScale guided reading: section 2
+ * names the block's shape but no positional encoding, bias or normalisation layout;
+ * section 4 names GeLU without its form).  All zero = pblock_forward.
+ *   gelu_tanh  0: exact erf GeLU;  1: the tanh approximation
+ *              z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) (Hendrycks and Gimpel,
+ *              "Gaussian Error Linear Units", section 2).
+ *   rope       0: no positional encoding;  1: rotary position embedding of q and k
+ *              (RoFormer, Su et al., section 3): in each head the pair of features
+ *              (2i, 2i+1) of the token at sequence position p (0-based, p = row mod S)
+ *              turns by the angle p * rope_base^(-2i/hd); v is not rotated.
+ *   rope_base  > 0 and finite when rope = 1 (10000 in RoFormer).
+ *   two_ln     0: one LayerNorm feeds both branches;  1: the MLP branch gets its own,
+ *              LN2 = (ln2_gamma, ln2_beta) of pblock_variant_weights. */
+typedef struct {
+  int32_t gelu_tanh;
+  int32_t rope;
+  float rope_base;
+  int32_t two_ln;
+} pblock_variant;
+
+/* Extra parameters of the variant forward, in the cfg's dtype, 16-byte aligned device
+ * memory owned by the caller; any may be NULL when unused:
+ *   b_in       [3*H*hd + ffn]  bias of the input projection, same row order as w_in
+ *              (added before the rotary embedding and before GeLU);
+ *   b_out      [d]             bias of the output projection (added once: the attention
+ *              out-projection and FC2 share one output);
+ *   ln2_gamma, ln2_beta  [d]   the MLP branch's LayerNorm (required when two_ln = 1). */
+typedef struct {
+  const void* b_in;
+  const void* b_out;
+  const void* ln2_gamma;
+  const void* ln2_beta;
+} pblock_variant_weights;
+
+/* The parallel block with the switches of `var`:
+ *   ua = LN(x),  um = ua or LN2(x)
+ *   [q|k|v] = ua W_qkv^T + b_in[:3A];  q, k rotated when rope = 1
+ *   f = um W_1^T + b_in[3A:]
+ *   y = [Attn_SWA(q, k, v) | GeLU(f)] W_out^T + b_out [+ x]
+ * vw may be NULL when no bias and no second LayerNorm is used; var must not be NULL
+ * (PBLOCK_ERR_NULL).  Switch values other than 0/1, or a bad rope_base, give
+ * PBLOCK_ERR_ARG.  With rope = 1 the cos/sin table for positions [0, B*S of the create
+ * cfg) is built in the handle's workspace (fp64, rounded to fp32) on `stream` the first
+ * time a base is used, and again whenever the base changes.  With two_ln = 1 the input
+ * GEMM runs as two launches around the second LayerNorm.  Stream, ownership, alignment,
+ * aliasing (out must not overlap the extra parameters either) and cfg rules as
+ * pblock_forward; per-kernel timing covers it like pblock_forward (a second LayerNorm
+ * counts as layernorm, both input GEMMs as gemm_in). */
+int pblock_forward_variant(pblock_t h, const void* x, const pblock_weights* w, const pblock_variant_weights* vw,
+                           const pblock_cfg* cfg, const pblock_variant* var, void* out, void* stream);
 
 /* Frees the workspace and the handle.  NULL is a no-op.  The caller must have
  * synchronised every stream the handle was used on. */

@@ -76,7 +76,8 @@ def test_workspace_and_flops():
         ws = tb.pblock_workspace_bytes(cfg)
         mt = -(-cfg.M // 256) * 256 + 256  # GEMM row operands u, AG: whole 256-row tiles plus one
         need = es * (mt * cfg.d + cfg.M * 3 * cfg.A + mt * cfg.k_out)
-        slack = 5 * 256
+        need += cfg.M * cfg.hd * 4  # rotary table: fp32 (cos, sin) for hd/2 pairs at M positions
+        slack = 6 * 256
         if cfg.dtype == "bf16":
             # GEMM scratch (host estimate at 256 CUs): one fp32 256x256 partial tile per CU
             need += 256 * 256 * 256 * 4
@@ -105,6 +106,9 @@ def test_null_arguments():
     assert lib.pblock_destroy(None) == _abi.PBLOCK_OK
     assert lib.pblock_set_timing(None, 1) == _abi.PBLOCK_ERR_NULL
     assert lib.pblock_copy_intermediates(None, None, None, None, None) == _abi.PBLOCK_ERR_NULL
+    var = tb.make_variant(rope=True)
+    assert lib.pblock_forward_variant(None, 16, ctypes.byref(w), None, ctypes.byref(c), ctypes.byref(var), 32,
+                                      None) == _abi.PBLOCK_ERR_NULL
 
 
 def test_attention_entry_rejects_before_device():

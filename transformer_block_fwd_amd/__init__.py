@@ -14,13 +14,22 @@ from __future__ import annotations
 import ctypes
 
 from . import _abi
-from ._abi import PBLOCK_BF16, PBLOCK_F32, PblockCfg, PblockError, PblockWeights  # noqa: F401
+from ._abi import (  # noqa: F401
+    PBLOCK_BF16,
+    PBLOCK_F32,
+    PblockCfg,
+    PblockError,
+    PblockVariant,
+    PblockVariantWeights,
+    PblockWeights,
+)
 
 __all__ = [
     "PBLOCK_BF16", "PBLOCK_F32", "PblockCfg", "PblockError", "PblockWeights", "ParallelBlock", "make_cfg",
     "pblock_validate_cfg", "pblock_workspace_bytes", "pblock_flops", "pblock_create", "pblock_forward",
     "pblock_destroy", "pblock_intermediates", "pblock_copy_intermediates", "pblock_set_timing",
     "pblock_kernel_times", "pblock_swa_attention", "pblock_strerror", "pblock_last_error", "KERNEL_NAMES",
+    "PblockVariant", "PblockVariantWeights", "make_variant", "pblock_forward_variant",
 ]
 
 KERNEL_NAMES = ("layernorm", "gemm_in", "attention", "gemm_out")
@@ -141,6 +150,33 @@ def pblock_forward_serial(handle: int, x, weights, ln2, cfg, out, stream=None) -
     _abi.check(_abi.lib().pblock_forward_serial(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), _ptr(gamma2),
                                                 _ptr(beta2), ctypes.byref(c), _ptr(out), _stream(stream)),
                "pblock_forward_serial")
+
+
+def make_variant(gelu_tanh=False, rope=False, rope_base=10000.0, two_ln=False) -> PblockVariant:
+    return PblockVariant(int(bool(gelu_tanh)), int(bool(rope)), float(rope_base), int(bool(two_ln)))
+
+
+def pblock_forward_variant(handle: int, x, weights, extra, cfg, variant, out, stream=None) -> None:
+    """The parallel block with the variant switches: weights = (ln_gamma, ln_beta, w_in, w_out),
+    extra = dict with any of b_in [3A+ffn], b_out [d], ln2_gamma [d], ln2_beta [d] (or None),
+    variant = a PblockVariant (see make_variant)."""
+    c = as_cfg(cfg)
+    gamma, beta, w_in, w_out = weights
+    extra = extra or {}
+    M, A = c.B * c.S, c.H * c.hd
+    for t, name, n in ((x, "x", M * c.d), (out, "out", M * c.d), (gamma, "ln_gamma", c.d), (beta, "ln_beta", c.d),
+                       (w_in, "w_in", (3 * A + c.ffn) * c.d), (w_out, "w_out", c.d * (A + c.ffn)),
+                       (extra.get("b_in"), "b_in", 3 * A + c.ffn), (extra.get("b_out"), "b_out", c.d),
+                       (extra.get("ln2_gamma"), "ln2_gamma", c.d), (extra.get("ln2_beta"), "ln2_beta", c.d)):
+        _check_tensor(t, name, c.dtype, n)
+    if not isinstance(variant, PblockVariant):
+        raise TypeError("variant must be a PblockVariant (make_variant)")
+    w = PblockWeights(_ptr(gamma), _ptr(beta), _ptr(w_in), _ptr(w_out))
+    vw = PblockVariantWeights(_ptr(extra.get("b_in")), _ptr(extra.get("b_out")), _ptr(extra.get("ln2_gamma")),
+                              _ptr(extra.get("ln2_beta")))
+    _abi.check(_abi.lib().pblock_forward_variant(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), ctypes.byref(vw),
+                                                 ctypes.byref(c), ctypes.byref(variant), _ptr(out), _stream(stream)),
+               "pblock_forward_variant")
 
 
 def _event_array(events, n, stream):

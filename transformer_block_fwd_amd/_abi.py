@@ -53,6 +53,24 @@ class PblockWeights(ctypes.Structure):
     ]
 
 
+class PblockVariant(ctypes.Structure):
+    _fields_ = [
+        ("gelu_tanh", ctypes.c_int32),
+        ("rope", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+        ("two_ln", ctypes.c_int32),
+    ]
+
+
+class PblockVariantWeights(ctypes.Structure):
+    _fields_ = [
+        ("b_in", ctypes.c_void_p),
+        ("b_out", ctypes.c_void_p),
+        ("ln2_gamma", ctypes.c_void_p),
+        ("ln2_beta", ctypes.c_void_p),
+    ]
+
+
 class PblockError(RuntimeError):
     def __init__(self, code: int, where: str, detail: str = ""):
         self.code = code
@@ -81,6 +99,9 @@ _SIGNATURES = {
     "pblock_forward_serial": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.c_void_p,
                                          _c.c_void_p, _c.POINTER(PblockCfg), _c.c_void_p, _c.c_void_p]),
     "pblock_mfma_loop": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
+    "pblock_forward_variant": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights),
+                                          _c.POINTER(PblockVariantWeights), _c.POINTER(PblockCfg),
+                                          _c.POINTER(PblockVariant), _c.c_void_p, _c.c_void_p]),
     "pblock_forward_chunked": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.POINTER(PblockCfg),
                                           _c.c_void_p, _c.c_int32, _c.POINTER(_c.c_void_p),
                                           _c.POINTER(_c.c_void_p), _c.c_void_p]),

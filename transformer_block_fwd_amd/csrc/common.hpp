@@ -66,4 +66,12 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return z * (z >= 0.0f ? 1.0f - h : h);
 }
 
+// GeLU's tanh approximation (Hendrycks and Gimpel, "Gaussian Error Linear Units", section 2):
+// z/2 (1 + tanh y), y = sqrt(2/pi) (z + 0.044715 z^3), evaluated as z * sigmoid(2y) =
+// z / (1 + 2^(-2y log2 e)); both tails are exact limits (2^+inf = inf gives -0 for z << 0).
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float y = 0.7978845608028654f * fmaf(0.044715f * z, z * z, z);
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.8853900817779268f * y));
+}
+
 }  // namespace pblk

@@ -54,10 +54,13 @@
 //     column off1 + (n - nsplit) (the FC1 activations next to the attention
 //     output, so the second GEMM reads one K-contiguous operand).
 //   kEpiResidual: optional residual x added in fp32, one rounding to bf16.
+// Optional variant steps, in fp32 before the rounding: a bias per column (first), the
+// rotary embedding of the q and k columns, the tanh form of GeLU.
 // nsplit, the strides and off1 are multiples of 8.
 #pragma once
 
 #include "common.hpp"
+#include "rope.hpp"
 
 namespace pblk {
 
@@ -75,6 +78,13 @@ struct GemmArgs {
   int nsplit;
   const uint16_t* resid;
   int64_t ldr;
+  // Variant switches of the epilogue (all off when zero / null):
+  const uint16_t* bias;  // [N] added to every row before anything else
+  const float* rope;     // (cos, sin) per (position, pair): rotary embedding of columns n < rope_n
+  int rope_n;            // columns [0, rope_n) are q and k heads of width hd
+  int seq;               // rows are sequences of seq positions (position = m % seq)
+  int hd;
+  int gelu_tanh;         // 1: tanh-form GeLU on the FC1 columns
 };
 
 constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 64, kGemmThreads = 256;
@@ -125,12 +135,26 @@ template <int EPI>
 __device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f32x4 lo, f32x4 hi) {
   float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   uint16_t* dst;
+  if (g.bias != nullptr) {
+    const u32x4 br = *reinterpret_cast<const u32x4*>(g.bias + n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] += __uint_as_float(br[e] << 16);
+      v[2 * e + 1] += __uint_as_float(br[e] & 0xFFFF0000u);
+    }
+  }
   if constexpr (EPI == kEpiSplitGelu) {
     if (n < g.nsplit) {
+      if (n < g.rope_n) rope_rotate8(v, g.rope, m % g.seq, n & (g.hd - 1), g.hd);
       dst = g.out0 + int64_t(m) * g.ld0 + n;
     } else {
+      if (g.gelu_tanh) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+        for (int e = 0; e < 8; ++e) v[e] = gelu_tanh(v[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+      }
       dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
     }
   } else {

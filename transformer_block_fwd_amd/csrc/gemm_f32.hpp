@@ -22,6 +22,11 @@ struct GemmArgsF32 {
   int nsplit;
   const float* resid;
   int64_t ldr;
+  // variant switches, as in the bf16 GEMM's epilogue (off when zero / null)
+  const float* bias;
+  const float* rope;
+  int rope_n, seq, hd;
+  int gelu_tanh;
 };
 
 // 64x64 tile, 256 threads, 4x4 outputs per thread, k slabs of 16 in LDS.
@@ -64,17 +69,36 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 g) {
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty * 4 + i;
     if (m >= g.M) continue;
+    const int nb = n0 + tx * 4;  // 4 consecutive columns, nb a multiple of 4; N is a multiple of 64
+    if (nb >= g.N) continue;
+    float v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
-      if (n >= g.N) continue;
-      float v = acc[i][j];
-      if constexpr (EPI == kEpiSplitGelu) {
-        if (n < g.nsplit) g.out0[int64_t(m) * g.ld0 + n] = v;
-        else g.out1[int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit)] = gelu_erf(v);
+    for (int j = 0; j < 4; ++j) v[j] = acc[i][j] + (g.bias != nullptr ? g.bias[nb + j] : 0.f);
+    if constexpr (EPI == kEpiSplitGelu) {
+      if (nb < g.nsplit) {
+        if (nb < g.rope_n) {
+          const int c = nb & (g.hd - 1);
+          const float* t = g.rope + (int64_t(m % g.seq) * (g.hd >> 1) + (c >> 1)) * 2;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float e = v[2 * q], o = v[2 * q + 1], cv = t[2 * q], sv = t[2 * q + 1];
+            v[2 * q] = e * cv - o * sv;
+            v[2 * q + 1] = e * sv + o * cv;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g.out0[int64_t(m) * g.ld0 + nb + j] = v[j];
       } else {
-        if (g.resid != nullptr) v += g.resid[int64_t(m) * g.ldr + n];
-        g.out0[int64_t(m) * g.ld0 + n] = v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          g.out1[int64_t(m) * g.ld1 + g.off1 + (nb + j - g.nsplit)] = g.gelu_tanh ? gelu_tanh(v[j]) : gelu_erf(v[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float r = v[j];
+        if (g.resid != nullptr) r += g.resid[int64_t(m) * g.ldr + nb + j];
+        g.out0[int64_t(m) * g.ld0 + nb + j] = r;
       }
     }
   }

@@ -8,6 +8,9 @@
 // The attention output and the GeLU activations share one K-contiguous buffer
 // (ag), so the out-projection and FC2 run as a single GEMM: the two branches
 // of the parallel block are summed inside its accumulators.
+// pblock_forward_variant runs the same launches with epilogue switches (biases,
+// rotary embedding of q and k, tanh GeLU), and with a second LayerNorm for the
+// MLP branch splits the input GEMM in two around it.
 #include <hip/hip_runtime.h>
 
 #include <array>
@@ -71,7 +74,7 @@ int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
 
 struct WsLayout {
-  int64_t u, qkv, ag, partials, total;
+  int64_t u, qkv, ag, partials, rope, total;
 };
 // G = persistent GEMM workgroups (the device's CU count); 0 for a host-only estimate at 256.
 WsLayout ws_layout(const pblock_cfg* c, int G) {
@@ -92,7 +95,9 @@ WsLayout ws_layout(const pblock_cfg* c, int G) {
     // the split-K tail holds at most G chunks (one wave)
     part_bytes = int64_t(G) * kGemmBM * kGemmBN * 4;
   }
-  w.total = w.partials + align256(part_bytes);
+  w.rope = w.partials + align256(part_bytes);
+  // rotary-embedding table: (cos, sin) fp32 for hd/2 pairs at positions 0 .. M-1 (any S <= M)
+  w.total = w.rope + align256(dm.M * c->hd * 4);
   return w;
 }
 
@@ -295,6 +300,7 @@ struct pblock_s {
   size_t ev_used;
   double ms_sum[kTimedKernels];
   int n_forwards;
+  double rope_base;  // base the rotary table in the workspace was built for (NaN: none yet)
 };
 
 namespace {
@@ -354,6 +360,7 @@ int check_forward(pblock_t h, const void* x, const pblock_weights* w, const pblo
 
 struct Ws {
   void *u, *qkv, *ag;
+  float* rope;
   SkScratch scr;
 };
 Ws workspace(pblock_s* h) {
@@ -362,6 +369,7 @@ Ws workspace(pblock_s* h) {
   w.u = base + h->lay.u;
   w.qkv = base + h->lay.qkv;
   w.ag = base + h->lay.ag;
+  w.rope = reinterpret_cast<float*>(base + h->lay.rope);
   w.scr.partials = reinterpret_cast<float*>(base + h->lay.partials);
   w.scr.G = h->n_cu;
   return w;
@@ -399,11 +407,21 @@ void run_layernorm(const void* x, const void* g, const void* b, void* u, int64_t
                      static_cast<float*>(u), M, c.d, c.ln_eps, s);
 }
 
+// Variant steps of the input GEMM's epilogue (all off by default).
+struct InEpi {
+  const void* bias = nullptr;  // [N] per output column
+  const float* rope = nullptr;  // rotary table; columns [0, rope_n) are q and k heads
+  int rope_n = 0;
+  int seq = 1;  // positions per sequence: row m is at position m % seq
+  int hd = 64;
+  int gelu_tanh = 0;
+};
+
 // out0[m, n] = Z[m, n] for n < nsplit; out1[m, off1 + n - nsplit] = GeLU(Z[m, n]) otherwise;
 // Z = A B^T, A [M, K] (row stride lda), B [N, K] (row stride ldb).
 void run_gemm_in(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M, int64_t N, int64_t K, void* out0,
                  int64_t ld0, void* out1, int64_t ld1, int64_t off1, int64_t nsplit, int dtype, const SkScratch& scr,
-                 hipStream_t s) {
+                 hipStream_t s, const InEpi& ep = InEpi{}) {
   if (dtype == PBLOCK_BF16) {
     GemmArgs g{};
     g.a = static_cast<const uint16_t*>(a); g.lda = lda;
@@ -412,6 +430,9 @@ void run_gemm_in(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t
     g.out0 = static_cast<uint16_t*>(out0); g.ld0 = ld0;
     g.out1 = static_cast<uint16_t*>(out1); g.ld1 = ld1; g.off1 = off1;
     g.nsplit = int(nsplit);
+    g.bias = static_cast<const uint16_t*>(ep.bias);
+    g.rope = ep.rope; g.rope_n = ep.rope_n; g.seq = ep.seq; g.hd = ep.hd;
+    g.gelu_tanh = ep.gelu_tanh;
     launch_gemm_bf16<kEpiSplitGelu>(g, scr, s);
   } else {
     GemmArgsF32 g{};
@@ -421,14 +442,17 @@ void run_gemm_in(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t
     g.out0 = static_cast<float*>(out0); g.ld0 = ld0;
     g.out1 = static_cast<float*>(out1); g.ld1 = ld1; g.off1 = off1;
     g.nsplit = int(nsplit);
+    g.bias = static_cast<const float*>(ep.bias);
+    g.rope = ep.rope; g.rope_n = ep.rope_n; g.seq = ep.seq; g.hd = ep.hd;
+    g.gelu_tanh = ep.gelu_tanh;
     launch_gemm_f32<kEpiSplitGelu>(g, s);
   }
 }
 
-// out [M, N] (row stride N) = A B^T (+ resid [M, N], row stride N); resid may be out itself
-// (each element is read by the thread that then writes it).
+// out [M, N] (row stride N) = A B^T (+ bias [N]) (+ resid [M, N], row stride N); resid may be
+// out itself (each element is read by the thread that then writes it).
 void run_gemm_out(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M, int64_t N, int64_t K, void* out,
-                  const void* resid, int dtype, const SkScratch& scr, hipStream_t s) {
+                  const void* resid, int dtype, const SkScratch& scr, hipStream_t s, const void* bias = nullptr) {
   if (dtype == PBLOCK_BF16) {
     GemmArgs g{};
     g.a = static_cast<const uint16_t*>(a); g.lda = lda;
@@ -436,6 +460,7 @@ void run_gemm_out(const void* a, int64_t lda, const void* b, int64_t ldb, int64_
     g.M = int(M); g.N = int(N); g.K = int(K);
     g.out0 = static_cast<uint16_t*>(out); g.ld0 = N;
     g.resid = static_cast<const uint16_t*>(resid); g.ldr = N;
+    g.bias = static_cast<const uint16_t*>(bias);
     launch_gemm_bf16<kEpiResidual>(g, scr, s);
   } else {
     GemmArgsF32 g{};
@@ -444,6 +469,7 @@ void run_gemm_out(const void* a, int64_t lda, const void* b, int64_t ldb, int64_
     g.M = int(M); g.N = int(N); g.K = int(K);
     g.out0 = static_cast<float*>(out); g.ld0 = N;
     g.resid = static_cast<const float*>(resid); g.ldr = N;
+    g.bias = static_cast<const float*>(bias);
     launch_gemm_f32<kEpiResidual>(g, s);
   }
 }
@@ -499,6 +525,7 @@ int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle) {
     h->timing = false;
     h->ev_used = 0;
     h->n_forwards = 0;
+    h->rope_base = std::nan("");
     for (double& v : h->ms_sum) v = 0.0;
     hipError_t e = hipMalloc(&h->ws, size_t(h->lay.total));
     if (e != hipSuccess) {
@@ -710,6 +737,88 @@ int pblock_forward_chunked(pblock_t h, const void* x, const pblock_weights* w, c
     }
     h->last_m = dm.M;
     return launch_status("pblock_forward_chunked launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int pblock_forward_variant(pblock_t h, const void* x, const pblock_weights* w, const pblock_variant_weights* vw,
+                           const pblock_cfg* cfg, const pblock_variant* var, void* out, void* stream) {
+  try {
+    Dims dm;
+    int st = check_forward(h, x, w, cfg, out, &dm);
+    if (st != PBLOCK_OK) return st;
+    const pblock_cfg& c = *cfg;
+    if (!var) return fail(PBLOCK_ERR_NULL, "variant is NULL");
+    const pblock_variant& v = *var;
+    if ((v.gelu_tanh != 0 && v.gelu_tanh != 1) || (v.rope != 0 && v.rope != 1) || (v.two_ln != 0 && v.two_ln != 1))
+      return fail(PBLOCK_ERR_ARG, "gelu_tanh, rope and two_ln must be 0 or 1");
+    if (v.rope && !(std::isfinite(v.rope_base) && v.rope_base > 0.f))
+      return fail(PBLOCK_ERR_ARG, "rope_base must be finite and > 0");
+    const pblock_variant_weights none{};
+    const pblock_variant_weights& e = vw ? *vw : none;
+    if (v.two_ln && (!e.ln2_gamma || !e.ln2_beta)) return fail(PBLOCK_ERR_NULL, "two_ln needs ln2_gamma and ln2_beta");
+    const int es = elem_size(c.dtype);
+    const int64_t xb = dm.M * c.d * es;
+    const void* ln2g = v.two_ln ? e.ln2_gamma : nullptr;
+    const void* ln2b = v.two_ln ? e.ln2_beta : nullptr;
+    const struct { const void* p; int64_t bytes; } extra[4] = {
+        {e.b_in, dm.n_in * es}, {e.b_out, int64_t(c.d) * es}, {ln2g, int64_t(c.d) * es}, {ln2b, int64_t(c.d) * es}};
+    for (const auto& t : extra) {
+      if (!t.p) continue;
+      if (!aligned16(t.p)) return fail(PBLOCK_ERR_ALIGN, "bias and LN2 pointers must be 16-byte aligned");
+      if (overlap(out, xb, t.p, t.bytes)) return fail(PBLOCK_ERR_ALIAS, "out overlaps a bias or an LN2 parameter");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Ws ws = workspace(h);
+    const int64_t A = dm.A;
+    if (v.rope && !(double(v.rope_base) == h->rope_base)) {
+      // (cos, sin) for every position the handle can see; rebuilt only when the base changes
+      const int64_t n = h->m_cap * (c.hd / 2);
+      hipLaunchKernelGGL(rope_table_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, ws.rope, int(h->m_cap),
+                         c.hd, double(v.rope_base));
+      st = launch_status("rope table launch");
+      if (st != PBLOCK_OK) return st;
+      h->rope_base = double(v.rope_base);
+    }
+    Timer tm;
+    st = tm.begin(h, s);
+    if (st != PBLOCK_OK) return st;
+    InEpi ep;
+    ep.bias = e.b_in;
+    ep.rope = v.rope ? ws.rope : nullptr;
+    ep.rope_n = v.rope ? int(2 * A) : 0;
+    ep.seq = c.S;
+    ep.hd = c.hd;
+    ep.gelu_tanh = v.gelu_tanh;
+    run_layernorm(x, w->ln_gamma, w->ln_beta, ws.u, dm.M, c, s);
+    tm.mark(0);
+    if (!v.two_ln) {
+      run_gemm_in(ws.u, c.d, w->w_in, c.d, dm.M, dm.n_in, c.d, ws.qkv, 3 * A, ws.ag, dm.k_out, A, 3 * A, c.dtype,
+                  ws.scr, s, ep);
+      tm.mark(1);
+    } else {
+      // the MLP branch has its own LayerNorm: q|k|v from LN(x), then FC1 from LN2(x) in the same u buffer
+      run_gemm_in(ws.u, c.d, w->w_in, c.d, dm.M, 3 * A, c.d, ws.qkv, 3 * A, nullptr, 0, 0, 3 * A, c.dtype, ws.scr, s,
+                  ep);
+      tm.mark(1);
+      run_layernorm(x, ln2g, ln2b, ws.u, dm.M, c, s);
+      tm.mark(0);
+      InEpi ep2 = ep;
+      ep2.bias = e.b_in ? static_cast<const char*>(e.b_in) + 3 * A * es : nullptr;
+      ep2.rope = nullptr;
+      ep2.rope_n = 0;
+      run_gemm_in(ws.u, c.d, static_cast<const char*>(w->w_in) + 3 * A * c.d * es, c.d, dm.M, c.ffn, c.d, nullptr, 0,
+                  ws.ag, dm.k_out, A, 0, c.dtype, ws.scr, s, ep2);
+      tm.mark(1);
+    }
+    launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
+    tm.mark(2);
+    run_gemm_out(ws.ag, dm.k_out, w->w_out, dm.k_out, dm.M, c.d, dm.k_out, out, c.add_residual ? x : nullptr, c.dtype,
+                 ws.scr, s, e.b_out);
+    tm.mark(3);
+    h->last_m = dm.M;
+    return launch_status("pblock_forward_variant launch");
   } catch (...) {
     return fail(PBLOCK_ERR_ARG, "internal error");
   }

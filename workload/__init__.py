@@ -197,6 +197,19 @@ def make_ln2(cfg: BlockConfig, seed: int = 0, affine: bool = False) -> dict[str,
     return dict(gamma2=gamma, beta2=beta, gamma2_dev=gamma, beta2_dev=beta)
 
 
+def make_variant_params(cfg: BlockConfig, seed: int = 0) -> dict[str, np.ndarray]:
+    """Biases of the two projections for the variant block, b_in [3A + ffn] and b_out [d],
+    each N(0, 0.1^2) from their own stream; float32 values as the device receives them under
+    "b_in"/"b_out" and the storage arrays under "b_in_dev"/"b_out_dev"."""
+    rng = np.random.Generator(np.random.PCG64([seed, 3]))
+    b_in = (0.1 * rng.standard_normal(cfg.n_in, dtype=np.float32)).astype(np.float32)
+    b_out = (0.1 * rng.standard_normal(cfg.d, dtype=np.float32)).astype(np.float32)
+    if cfg.dtype == "bf16":
+        (bi, bid), (bo, bod) = round_to_bf16(b_in), round_to_bf16(b_out)
+        return dict(b_in=bi, b_out=bo, b_in_dev=bid, b_out_dev=bod)
+    return dict(b_in=b_in, b_out=b_out, b_in_dev=b_in, b_out_dev=b_out)
+
+
 def sample_row_blocks(cfg: BlockConfig, block: int = 32, seed: int = 1) -> list[tuple[int, int, int]]:
     """Query row blocks (b, i0, i1) for sampled checks at full size.
 
