@@ -37,8 +37,9 @@ COLD_SCRUB_MIB = 512       # written between cold-cache steps (more than the 256
 # per launch; None until measured for the current kernel build.
 MEASURED_TRAFFIC_BYTES = {
     # gemm_in main kernel + its split-K tail reduce (profiles/shard175b_kernels.md); set
-    # only for the GEMM build the counters were taken on (4-wave 128x128, 64-deep slabs, row-major split-K partials)
-    "shard175b": 1025523438,
+    # only for the GEMM build the counters were taken on (4-wave 128x128, 64-deep slabs, row-major split-K
+    # partials, epilogue with the variant steps)
+    "shard175b": 1036577090,
 }
 
 WORKLOAD_NOTES = {
