@@ -37,7 +37,10 @@ the comparison of the two forms (section 2 contrasts them; section 8's ablation
 prices the parallel form); "standard layer" is read as the pre-LN layout.  So
 are the alternatives to the silent choices above, as explicit switches of
 block_forward_variant: the tanh GeLU, linear biases, rotary position embedding
-of q and k (RoFormer), and a second LayerNorm for the MLP branch.
+of q and k (RoFormer), and a second LayerNorm for the MLP branch.  And so is
+the backward pass of the block (section 3: what is done in the forward pass is
+done in the backward pass too): block_backward, the chain rule through every
+step, with the softmax Jacobian written out.
 
 Pins (all in the CPU test-suite): dense brute-force band attention, W >= S vs
 torch's causal attention, W = 1 closed form, 2-key closed form, the branch-sum
@@ -47,7 +50,10 @@ against torch library routines and, with one sub-layer switched off, against
 the parallel block; the variant switches against torch library routines
 (layer_norm, linear with bias, tanh gelu) with the rotation done as complex
 multiplication, RoPE's dependence on relative position only, hand-computed
-rotations, and reduction to block_forward with every switch off.
+rotations, and reduction to block_forward with every switch off; the backward
+pass against torch autograd in float64, central finite differences, the zero
+gradient of q and k at W = 1, LayerNorm's shift and scale invariance, and the
+GeLU derivative against torch.
 """
 from __future__ import annotations
 
@@ -234,6 +240,111 @@ def serial_block_forward_rows(x, gamma, beta, gamma2, beta2, w_in, w_out, H: int
         u2 = layer_norm(h, gamma2, beta2, eps)
         outs.append(h + gelu(u2 @ w_in[3 * A:].T) @ w_out[:, A:].T)
     return outs
+
+
+# ----------------------------------------------------------------------------- backward pass
+# The pages' context is training ("the same is done in the backward pass", section 3): the
+# gradients of the block's loss with respect to its input and parameters, given the gradient
+# dy of its output, by the chain rule through each step of block_forward.
+
+
+def gelu_grad(z):
+    """d/dz of the exact GeLU z * Phi(z): Phi(z) + z * phi(z), phi the standard normal density."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * (1.0 + erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def swa_attention_backward(q, k, v, do, W: int, slab: int = 128):
+    """Gradients of swa_attention(q, k, v, W) for one sequence given the output gradient do.
+
+    With s_ij = q_i.k_j / sqrt(hd) on the band and p_i = softmax(s_i): dp_ij = do_i.v_j,
+    ds_ij = p_ij (dp_ij - sum_l p_il dp_il) (the softmax Jacobian), dq_i = sum_j ds_ij k_j /
+    sqrt(hd), dk_j = sum_i ds_ij q_i / sqrt(hd), dv_j = sum_i p_ij do_i.  Returns dq, dk, dv,
+    each [S, H, hd]; slabs of queries meet only the keys their windows reach.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    S, H, hd = q.shape
+    scale = 1.0 / math.sqrt(hd)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for s0 in range(0, S, slab):
+        s1 = min(S, s0 + slab)
+        j0 = window_lo(s0, W)
+        j1 = s1 - 1
+        qi = np.arange(s0, s1)[:, None]
+        kj = np.arange(j0, j1 + 1)[None, :]
+        allowed = (kj <= qi) & (kj >= qi - W + 1)
+        qs = q[s0:s1].transpose(1, 0, 2)  # [H, n, hd]
+        kk = k[j0:j1 + 1].transpose(1, 0, 2)  # [H, L, hd]
+        vv = v[j0:j1 + 1].transpose(1, 0, 2)
+        dos = do[s0:s1].transpose(1, 0, 2)
+        scores = np.where(allowed[None], (qs @ kk.transpose(0, 2, 1)) * scale, -np.inf)
+        p = np.exp(scores - scores.max(axis=-1, keepdims=True))
+        p /= p.sum(axis=-1, keepdims=True)  # [H, n, L], zero outside the band
+        dp = dos @ vv.transpose(0, 2, 1)
+        ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+        dq[s0:s1] += (ds @ kk).transpose(1, 0, 2) * scale
+        dk[j0:j1 + 1] += (ds.transpose(0, 2, 1) @ qs).transpose(1, 0, 2) * scale
+        dv[j0:j1 + 1] += (p.transpose(0, 2, 1) @ dos).transpose(1, 0, 2)
+    return dq, dk, dv
+
+
+def layer_norm_backward(x, gamma, du, eps: float):
+    """Gradients of u = (x - mu) / sigma * gamma + beta (sigma = sqrt(biased var + eps)) over
+    the last axis: dx = (g - mean(g) - xhat * mean(g * xhat)) / sigma with g = du * gamma,
+    dgamma = sum(du * xhat), dbeta = sum(du) over all rows."""
+    x = np.asarray(x, np.float64)
+    du = np.asarray(du, np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    sigma = np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+    xhat = (x - mu) / sigma
+    g = du * np.asarray(gamma, np.float64)
+    dx = (g - g.mean(axis=-1, keepdims=True) - xhat * (g * xhat).mean(axis=-1, keepdims=True)) / sigma
+    lead = tuple(range(du.ndim - 1))
+    return dx, (du * xhat).sum(axis=lead), du.sum(axis=lead)
+
+
+def block_backward(x, gamma, beta, w_in, w_out, dy, H: int, hd: int, W: int, eps: float = 1e-5,
+                   add_residual: bool = True):
+    """Gradients of block_forward with respect to x, gamma, beta, W_in and W_out given dy
+    [B, S, d].  Returns a dict with dx [B, S, d], dgamma [d], dbeta [d], dw_in
+    [3A + ffn, d], dw_out [d, A + ffn]."""
+    x = np.asarray(x, np.float64)
+    w_in = np.asarray(w_in, np.float64)
+    w_out = np.asarray(w_out, np.float64)
+    dy = np.asarray(dy, np.float64)
+    B, S, d = x.shape
+    A = H * hd
+    # forward, keeping what the chain rule needs
+    u = layer_norm(x, gamma, beta, eps)
+    z = u @ w_in.T
+    q, k, v, f = split_projection(z, H, hd)
+    o = np.empty((B, S, H, hd))
+    for b in range(B):
+        o[b] = swa_attention(q[b], k[b], v[b], W)
+    ag = np.concatenate([o.reshape(B, S, A), gelu(f)], axis=-1)
+    # y = ag W_out^T (+ x)
+    dw_out = dy.reshape(-1, d).T @ ag.reshape(-1, ag.shape[-1])
+    dag = dy @ w_out
+    do = dag[..., :A].reshape(B, S, H, hd)
+    df = dag[..., A:] * gelu_grad(f)
+    dz = np.empty_like(z)
+    for b in range(B):
+        dq, dk, dv = swa_attention_backward(q[b], k[b], v[b], do[b], W)
+        dz[b, :, 0:A] = dq.reshape(S, A)
+        dz[b, :, A:2 * A] = dk.reshape(S, A)
+        dz[b, :, 2 * A:3 * A] = dv.reshape(S, A)
+    dz[..., 3 * A:] = df
+    dw_in = dz.reshape(-1, z.shape[-1]).T @ u.reshape(-1, d)
+    du = dz @ w_in
+    dx, dgamma, dbeta = layer_norm_backward(x, gamma, du, eps)
+    if add_residual:
+        dx = dx + dy
+    return dict(dx=dx, dgamma=dgamma, dbeta=dbeta, dw_in=dw_in, dw_out=dw_out)
 
 
 # ----------------------------------------------------------------------------- variant knobs

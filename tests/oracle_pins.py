@@ -15,7 +15,10 @@ reference values come from, in turn:
   * for the variant switches: torch's linear-with-bias and tanh gelu, the rotary
     embedding as complex multiplication (RoFormer's complex form), rotations of
     basis vectors worked out by hand, and RoPE's dependence on relative position
-    only.
+    only;
+  * for the backward pass: torch autograd in float64, central finite
+    differences of the (separately pinned) forward, LayerNorm's shift and scale
+    invariance, and the exactly zero q/k gradients at W = 1.
 """
 from __future__ import annotations
 
@@ -544,6 +547,136 @@ def pin_variant_rows_match_full(ob):
         np.testing.assert_allclose(y, full[bb, i0:i1], rtol=1e-12, atol=1e-13)
 
 
+# ----------------------------------------------------------------------------- backward pass
+
+
+def _torch_block_grads(x, g, b, wi, wo, H, hd, W, eps, dy, add_residual=True):
+    """Gradients of sum(dy * block(x)) by torch autograd through float64 library routines."""
+    t = {k: torch.from_numpy(np.array(v)).requires_grad_(True) for k, v in
+         dict(x=x, gamma=g, beta=b, w_in=wi, w_out=wo).items()}
+    B, S, d = x.shape
+    A = H * hd
+    u = F.layer_norm(t["x"], (d,), t["gamma"], t["beta"], eps)
+    z = u @ t["w_in"].T
+    q, k, v = (z[..., c * A:(c + 1) * A].reshape(B, S, H, hd).transpose(1, 2) for c in range(3))
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=(j <= i) & (j > i - W)).transpose(1, 2).reshape(B, S, A)
+    y = torch.cat([o, F.gelu(z[..., 3 * A:], approximate="none")], dim=-1) @ t["w_out"].T
+    if add_residual:
+        y = y + t["x"]
+    (y * torch.from_numpy(dy)).sum().backward()
+    return dict(dx=t["x"].grad.numpy(), dgamma=t["gamma"].grad.numpy(), dbeta=t["beta"].grad.numpy(),
+                dw_in=t["w_in"].grad.numpy(), dw_out=t["w_out"].grad.numpy())
+
+
+def pin_gelu_grad(ob):
+    """GeLU derivative == torch autograd of the exact gelu and central differences of x*Phi(x)."""
+    z = np.linspace(-8, 8, 1601)
+    tz = torch.from_numpy(z).requires_grad_(True)
+    F.gelu(tz, approximate="none").sum().backward()
+    np.testing.assert_allclose(ob.gelu_grad(z), tz.grad.numpy(), rtol=1e-12, atol=1e-14)
+    h = 1e-5
+    fd = np.array([((t + h) * 0.5 * (1 + math.erf((t + h) / math.sqrt(2)))
+                    - (t - h) * 0.5 * (1 + math.erf((t - h) / math.sqrt(2)))) / (2 * h) for t in z])
+    np.testing.assert_allclose(ob.gelu_grad(z), fd, rtol=0, atol=1e-8)
+
+
+def pin_layer_norm_backward(ob):
+    """LayerNorm backward == torch autograd; dx of the normalisation is orthogonal to the
+    all-ones vector (shift invariance) and, with eps = 0, to xhat (scale invariance), row
+    by row."""
+    rng = _rng(131)
+    x = rng.standard_normal((3, 5, 24)) * 2.0 + 1.0
+    g = 1.0 + 0.3 * rng.standard_normal(24)
+    b = 0.2 * rng.standard_normal(24)
+    du = rng.standard_normal((3, 5, 24))
+    tx, tg, tb = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (x, g, b))
+    (F.layer_norm(tx, (24,), tg, tb, 1e-5) * torch.from_numpy(du)).sum().backward()
+    dx, dg, db = ob.layer_norm_backward(x, g, du, 1e-5)
+    np.testing.assert_allclose(dx, tx.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dg, tg.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(db, tb.grad.numpy(), rtol=1e-11, atol=1e-12)
+    # shift invariance holds for any eps; scale invariance only without eps
+    np.testing.assert_allclose(dx.sum(-1), 0.0, atol=1e-11)
+    dx0, _, _ = ob.layer_norm_backward(x, g, du, 0.0)
+    xhat = (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, keepdims=True))
+    np.testing.assert_allclose(dx0.sum(-1), 0.0, atol=1e-11)
+    np.testing.assert_allclose((dx0 * xhat).sum(-1), 0.0, atol=1e-11)
+
+
+def pin_attention_backward(ob):
+    """Band attention backward == torch autograd through band-masked SDPA (odd S, several
+    W); at W = 1 dq = dk = 0 and dv = do exactly."""
+    rng = _rng(141)
+    for S, H, hd, W in ((37, 2, 8, 5), (70, 1, 16, 70), (133, 2, 4, 17)):
+        q, k, v, do = (rng.standard_normal((S, H, hd)) for _ in range(4))
+        tq, tk, tv = (torch.from_numpy(a.transpose(1, 0, 2).copy()).requires_grad_(True) for a in (q, k, v))
+        i = torch.arange(S)[:, None]
+        j = torch.arange(S)[None, :]
+        o = F.scaled_dot_product_attention(tq[None], tk[None], tv[None], attn_mask=(j <= i) & (j > i - W))[0]
+        (o * torch.from_numpy(do.transpose(1, 0, 2).copy())).sum().backward()
+        dq, dk, dv = ob.swa_attention_backward(q, k, v, do, W)
+        for got, ref in ((dq, tq), (dk, tk), (dv, tv)):
+            np.testing.assert_allclose(got, ref.grad.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-11)
+    q, k, v, do = (rng.standard_normal((20, 2, 8)) for _ in range(4))
+    dq, dk, dv = ob.swa_attention_backward(q, k, v, do, 1)
+    assert np.abs(dq).max() == 0.0 and np.abs(dk).max() == 0.0
+    np.testing.assert_allclose(dv, do, rtol=0, atol=1e-15)
+
+
+def pin_block_backward_vs_autograd(ob):
+    """Whole-block gradients == torch autograd (odd shapes, several W, with and without the
+    residual, random gamma/beta)."""
+    for seed, (B, S, d, H, hd, ffn), W in ((151, (2, 45, 24, 3, 8, 40), 9),
+                                           (152, (1, 70, 32, 2, 16, 48), 70),
+                                           (153, (3, 17, 16, 1, 8, 8), 1)):
+        x, g, b, wi, wo = _rand_block(seed, B, S, d, H, hd, ffn)
+        dy = _rng(seed + 7).standard_normal(x.shape)
+        for add_res in (True, False):
+            got = ob.block_backward(x, g, b, wi, wo, dy, H, hd, W, eps=1e-5, add_residual=add_res)
+            ref = _torch_block_grads(x, g, b, wi, wo, H, hd, W, 1e-5, dy, add_res)
+            for key in ref:
+                np.testing.assert_allclose(got[key], ref[key], rtol=1e-9, atol=1e-10, err_msg=key)
+
+
+def pin_block_backward_finite_differences(ob):
+    """<gradient, direction> == central difference of sum(dy * block_forward) along random
+    directions of each input and parameter (the forward is pinned on its own)."""
+    B, S, d, H, hd, ffn, W = 1, 19, 16, 2, 4, 24, 6
+    x, g, b, wi, wo = _rand_block(161, B, S, d, H, hd, ffn)
+    rng = _rng(162)
+    dy = rng.standard_normal(x.shape)
+    grads = ob.block_backward(x, g, b, wi, wo, dy, H, hd, W)
+    params = dict(x=x, gamma=g, beta=b, w_in=wi, w_out=wo)
+    names = dict(x="dx", gamma="dgamma", beta="dbeta", w_in="dw_in", w_out="dw_out")
+
+    def loss(p):
+        return float((dy * ob.block_forward(p["x"], p["gamma"], p["beta"], p["w_in"], p["w_out"], H, hd, W)).sum())
+
+    eps = 1e-6
+    for name, val in params.items():
+        for _ in range(2):
+            direction = rng.standard_normal(val.shape)
+            plus = dict(params, **{name: val + eps * direction})
+            minus = dict(params, **{name: val - eps * direction})
+            fd = (loss(plus) - loss(minus)) / (2 * eps)
+            an = float((grads[names[name]] * direction).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def pin_block_backward_w1(ob):
+    """At W = 1 every token attends to itself only, so the loss does not depend on q or k:
+    the W_in rows of Q and K get exactly zero gradient, those of V and FC1 do not."""
+    B, S, d, H, hd, ffn = 2, 13, 16, 2, 8, 24
+    x, g, b, wi, wo = _rand_block(171, B, S, d, H, hd, ffn)
+    dy = _rng(172).standard_normal(x.shape)
+    dw_in = ob.block_backward(x, g, b, wi, wo, dy, H, hd, 1)["dw_in"]
+    A = H * hd
+    assert np.abs(dw_in[:2 * A]).max() == 0.0
+    assert np.abs(dw_in[2 * A:3 * A]).min() > 0.0 and np.abs(dw_in[3 * A:]).max() > 1e-3
+
+
 ALL_PINS = [
     pin_attention_brute_force,
     pin_attention_vs_torch_band,
@@ -569,4 +702,10 @@ ALL_PINS = [
     pin_variant_vs_torch,
     pin_variant_reductions,
     pin_variant_rows_match_full,
+    pin_gelu_grad,
+    pin_layer_norm_backward,
+    pin_attention_backward,
+    pin_block_backward_vs_autograd,
+    pin_block_backward_finite_differences,
+    pin_block_backward_w1,
 ]

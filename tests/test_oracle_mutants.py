@@ -57,6 +57,20 @@ MUTANTS = {
     "bias_in_skips_mlp": [("f = f + b_in[3 * A:]", "f = f")],
     "bias_out_dropped": [("y = y + b_out", "y = y")],
     "two_ln_swapped": [("z = u_attn @ w_in[:3 * A].T", "z = u_mlp @ w_in[:3 * A].T")],
+    "gelu_grad_no_density_term": [(" + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)", "")],
+    "softmax_bwd_not_centred": [("ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))", "ds = p * dp")],
+    "dq_missing_scale": [("dq[s0:s1] += (ds @ kk).transpose(1, 0, 2) * scale", "dq[s0:s1] += (ds @ kk).transpose(1, 0, 2)")],
+    "dv_from_ds": [("dv[j0:j1 + 1] += (p.transpose(0, 2, 1) @ dos)", "dv[j0:j1 + 1] += (ds.transpose(0, 2, 1) @ dos)")],
+    "dk_dv_swapped": [("dz[b, :, A:2 * A] = dk.reshape(S, A)", "dz[b, :, A:2 * A] = dv.reshape(S, A)"),
+                      ("dz[b, :, 2 * A:3 * A] = dv.reshape(S, A)", "dz[b, :, 2 * A:3 * A] = dk.reshape(S, A)")],
+    "ln_bwd_no_xhat_term": [(" - xhat * (g * xhat).mean(axis=-1, keepdims=True)", "")],
+    "ln_bwd_dgamma_without_xhat": [("return dx, (du * xhat).sum(axis=lead), du.sum(axis=lead)",
+                                    "return dx, du.sum(axis=lead), du.sum(axis=lead)")],
+    "residual_grad_dropped": [("        dx = dx + dy\n", "        dx = dx\n")],
+    "dw_out_before_gelu": [("dw_out = dy.reshape(-1, d).T @ ag.reshape(-1, ag.shape[-1])",
+                            "dw_out = dy.reshape(-1, d).T @ np.concatenate([o.reshape(B, S, A), f], axis=-1).reshape(-1, ag.shape[-1])")],
+    "dw_in_from_x": [("dw_in = dz.reshape(-1, z.shape[-1]).T @ u.reshape(-1, d)",
+                      "dw_in = dz.reshape(-1, z.shape[-1]).T @ x.reshape(-1, d)")],
 }
 
 
