@@ -16,6 +16,7 @@ run, and the fp64 CPU oracle timed on the host as a baseline.
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload shard175b]
                   [--block parallel|serial] [--window W] [--chunks N]
                   [--gelu-tanh] [--bias] [--rope BASE] [--two-ln]   # variant switches
+                  [--train]    # forward with saved activations + backward pass
   python bench.py --sweep      # attention time against window and sequence length
 """
 from __future__ import annotations
@@ -27,6 +28,7 @@ import sys
 import time
 
 METRIC = "parallel-block fwd TFLOP/s and % of bf16 MFMA peak; tokens/s (1 GPU)"
+METRIC_TRAIN = "parallel-block training step (fwd + bwd) TFLOP/s and % of bf16 MFMA peak; tokens/s (1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
 DEFAULT_WORKLOAD = "shard175b"
@@ -69,6 +71,8 @@ def parse():
     p.add_argument("--rope", type=float, default=0.0, metavar="BASE",
                    help="variant: rotary embedding of q and k with this base (0: off)")
     p.add_argument("--two-ln", action="store_true", help="variant: a second LayerNorm for the MLP branch")
+    p.add_argument("--train", action="store_true",
+                   help="time a training step: the forward that saves activations plus the backward pass")
     p.add_argument("--cold-steps", type=int, default=10, help="cold-cache steps after the timed run (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -90,7 +94,13 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
 
 
-def cpu_baseline(cfg, inp, block, ln2, variant=None) -> dict:
+def backward_flops(cfg) -> float:
+    """Algorithmic FLOPs of the backward pass: each GEMM twice (input and weight gradients) and
+    the attention backward at 2.5x its forward (dV, dP, dQ, dK and the recomputed scores)."""
+    return 2.0 * (cfg.gemm1_flops() + cfg.gemm2_flops()) + 2.5 * cfg.attn_flops()
+
+
+def cpu_baseline(cfg, inp, block, ln2, variant=None, train_dy=None) -> dict:
     """The fp64 oracle, as it stands, timed once on the host cores over the whole workload."""
     import oracle
 
@@ -101,6 +111,14 @@ def cpu_baseline(cfg, inp, block, ln2, variant=None) -> dict:
     except Exception:  # noqa: BLE001
         threads = os.cpu_count() or 1
     t0 = time.perf_counter()
+    if train_dy is not None:
+        oracle.block_backward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, train_dy, cfg.H, cfg.hd, cfg.W,
+                              eps=cfg.ln_eps, add_residual=bool(cfg.add_residual))
+        dt = time.perf_counter() - t0
+        fl = cfg.flops() + backward_flops(cfg)
+        return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                "seconds": round(dt, 3), "tokens_per_s": round(cfg.M / dt, 1),
+                "sample": f"one full forward + backward of the {cfg.name} workload (all {cfg.M} tokens), float64 numpy"}
     if block == "serial":
         oracle.serial_block_forward(inp.x, inp.gamma, inp.beta, ln2["gamma2"], ln2["beta2"], inp.w_in, inp.w_out,
                                     cfg.H, cfg.hd, cfg.W, eps=cfg.ln_eps)
@@ -207,7 +225,7 @@ def main():
     import torch
 
     import transformer_block_fwd_amd as tb
-    from workload import CONFIGS, make_inputs, make_ln2, make_variant_params
+    from workload import CONFIGS, make_dy, make_inputs, make_ln2, make_variant_params
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -262,9 +280,23 @@ def main():
         if args.two_ln:
             oracle_variant.update(gamma2=ln2["gamma2"], beta2=ln2["beta2"])
     done = [torch.cuda.Event(enable_timing=True) for _ in range(args.chunks)]
+    train_dy = None
+    if args.train:
+        if args.block != "parallel" or use_variant or args.chunks or cfg.dtype != "bf16":
+            raise SystemExit("--train times the plain bf16 parallel block")
+        dyd = make_dy(cfg, seed=0)
+        train_dy = dyd["dy"]
+        dy_dev = torch.from_numpy(np.ascontiguousarray(dyd["dy_dev"]).view(np.int16)).view(torch.bfloat16).cuda()
+        train_ws = torch.empty(tb.pblock_train_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+        grads = {"dx": torch.empty_like(dev["x"]), "dln_gamma": torch.empty_like(dev["gamma"]),
+                 "dln_beta": torch.empty_like(dev["beta"]), "dw_in": torch.empty_like(dev["w_in"]),
+                 "dw_out": torch.empty_like(dev["w_out"])}
 
     def step(chunked=bool(args.chunks)):
-        if args.block == "serial":
+        if args.train:
+            tb.pblock_forward_train(h, dev["x"], weights, cfg, out, train_ws, stream)
+            tb.pblock_backward(h, dev["x"], weights, cfg, dy_dev, grads, train_ws, stream)
+        elif args.block == "serial":
             tb.pblock_forward_serial(h, dev["x"], weights, (dev["gamma2"], dev["beta2"]), cfg, out, stream)
         elif use_variant:
             tb.pblock_forward_variant(h, dev["x"], weights, extra, cfg, variant, out, stream)
@@ -290,7 +322,9 @@ def main():
     wall = time.perf_counter() - t_wall
     ms_total = marks[0].elapsed_time(marks[-1])
     step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
-    kernel_ms, n_fwd = tb.pblock_kernel_times(h)
+    kernel_ms, n_fwd = tb.pblock_kernel_times(h, backward=args.train)
+    if args.train:
+        n_fwd //= 2  # a forward and a backward call per step
     tb.pblock_set_timing(h, False)
     print(f"[bench] timed {args.steps} steps in {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms)", file=sys.stderr,
           flush=True)
@@ -352,13 +386,13 @@ def main():
     print(f"[bench] register-only MFMA loop {mfma_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     ms_step = ms_total / args.steps
-    flops = cfg.flops()
+    flops = cfg.flops() + (backward_flops(cfg) if args.train else 0.0)
     tflops = flops / (ms_step * 1e-3) / 1e12
     k_avg = {k: v / max(n_fwd, 1) for k, v in kernel_ms.items()}
     g1_ms = k_avg["gemm_in"]
     g1_flops = cfg.gemm1_flops()
     as_profiled = (args.block == "parallel" and not args.window and args.add_residual is None and not args.chunks
-                   and not use_variant)
+                   and not use_variant and not args.train)
     traffic = MEASURED_TRAFFIC_BYTES.get(cfg.name) if as_profiled else None
     roofline = {"kernel": "gemm_in (fused QKV+FC1 GEMM, GeLU epilogue)", "bound": "mfma",
                 "achieved": round(g1_flops / (g1_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -368,7 +402,10 @@ def main():
         roofline["kernel"] = "gemm_in (QKV GEMM + FC1 GEMM with GeLU epilogue, summed per forward)"
     per_kernel = {}
     for k, ms in k_avg.items():
-        kf = {"gemm_in": cfg.gemm1_flops(), "gemm_out": cfg.gemm2_flops(), "attention": cfg.attn_flops()}.get(k)
+        kf = {"gemm_in": cfg.gemm1_flops(), "gemm_out": cfg.gemm2_flops(), "attention": cfg.attn_flops(),
+              "bwd_gemm_dgrad": cfg.gemm1_flops() + cfg.gemm2_flops(),
+              "bwd_gemm_wgrad": cfg.gemm1_flops() + cfg.gemm2_flops(),
+              "bwd_attention": 2.5 * cfg.attn_flops()}.get(k)
         rec = {"ms": round(ms, 5)}
         if kf:
             rec["tflops"] = round(kf / (ms * 1e-3) / 1e12, 2)
@@ -380,7 +417,7 @@ def main():
         per_kernel[k] = rec
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if not args.train else METRIC_TRAIN,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -394,7 +431,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
         "config": {"workload": f"{cfg.name}: {WORKLOAD_NOTES.get(cfg.name, '')}", "block": args.block, "B": cfg.B,
                    "S": cfg.S, "d": cfg.d, "H": cfg.H, "hd": cfg.hd, "ffn": cfg.ffn, "W": cfg.W,
-                   "add_residual": cfg.add_residual, "parallelism": "single GPU", "variant": variant_desc},
+                   "add_residual": cfg.add_residual, "parallelism": "single GPU", "variant": variant_desc,
+                   "step": "forward + backward" if args.train else "forward"},
         "pct_peak_bf16": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.M / (ms_step * 1e-3), 1),
         "algorithmic_gflop_per_step": round(flops / 1e9, 3),
@@ -412,7 +450,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.block, ln2, oracle_variant)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.block, ln2, oracle_variant, train_dy)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

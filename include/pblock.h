@@ -209,6 +209,43 @@ typedef struct {
 int pblock_forward_variant(pblock_t h, const void* x, const pblock_weights* w, const pblock_variant_weights* vw,
                            const pblock_cfg* cfg, const pblock_variant* var, void* out, void* stream);
 
+/* ---- Training: forward with saved activations, and the backward pass ----
+ * The pages' setting is training; the backward pass mirrors the forward (MegaScale guided
+ * reading, section 3: what the parallel block and the overlap do in the forward pass "is
+ * done in the backward pass" too).  Gradients of L = sum(dy * y) by the chain rule through
+ * LayerNorm, the input projection, the sliding-window softmax attention (FlashAttention-2
+ * style: softmax weights recomputed from the saved log-sum-exp), GeLU and the output
+ * projection.  bf16 only (PBLOCK_ERR_DTYPE otherwise), d <= 16384 (PBLOCK_ERR_SHAPE).
+ *
+ * The training workspace is caller-owned device memory, 256-byte aligned, of at least
+ * pblock_train_workspace_bytes(cfg) bytes.  It holds the activations the forward saves
+ * (u, q|k|v, [attention | GeLU], the FC1 pre-activation, the per-query log-sum-exp) and the
+ * backward's scratch (transposed weights and activations, dz, du, LayerNorm partial sums).
+ * pblock_forward_train and the pblock_backward that consumes it must get the same cfg, x and
+ * weights, and the workspace must not be touched in between. */
+typedef struct {
+  void* dx;         /* [B, S, d]           dL/dx (includes dy when cfg->add_residual = 1) */
+  void* dln_gamma;  /* [d] */
+  void* dln_beta;   /* [d] */
+  void* dw_in;      /* [3*H*hd + ffn, d]   same layout as w_in */
+  void* dw_out;     /* [d, H*hd + ffn]     same layout as w_out */
+} pblock_grads;
+
+/* Bytes of training workspace for cfg (host only), or a negative status. */
+int64_t pblock_train_workspace_bytes(const pblock_cfg* cfg);
+
+/* pblock_forward's result in out, plus the saved activations in ws (ws_bytes long).  Rules as
+ * pblock_forward; out must not overlap ws, and ws must not overlap x or a weight. */
+int pblock_forward_train(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out,
+                         void* ws, int64_t ws_bytes, void* stream);
+
+/* Gradients for the output gradient dy [B, S, d] of the forward that pblock_forward_train saved
+ * in ws: every pointer of *grads is written (fp32 accumulation, one bf16 rounding of each
+ * result; dx, dgamma and dbeta see du in fp32).  The gradients must not overlap each other,
+ * x, dy, a weight or ws (PBLOCK_ERR_ALIAS); all 16-byte aligned.  Enqueued on `stream`. */
+int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, const void* dy,
+                    const pblock_grads* grads, void* ws, int64_t ws_bytes, void* stream);
+
 /* Frees the workspace and the handle.  NULL is a no-op.  The caller must have
  * synchronised every stream the handle was used on. */
 int pblock_destroy(pblock_t h);
@@ -233,14 +270,16 @@ int pblock_intermediates(pblock_t h, void** u, void** qkv, void** ag);
  * has run on the handle. */
 int pblock_copy_intermediates(pblock_t h, void* u, void* qkv, void* ag, void* stream);
 
-/* Per-kernel timing.  When enabled, pblock_forward and pblock_forward_serial
- * record HIP events around each of their launches on the forward's stream;
- * pblock_kernel_times then synchronises on the last recorded event and returns
- * the summed milliseconds per kernel since the last reset, in the order
- * [layernorm, gemm_in, attention, gemm_out], plus the number of forwards timed
- * (the serial form's two LayerNorms count as layernorm, its QKV and FC1 GEMMs
- * as gemm_in, its output-projection and FC2 GEMMs as gemm_out).  Enabling or
- * disabling resets the sums.  n must be >= 4. */
+/* Per-kernel timing.  When enabled, pblock_forward, pblock_forward_serial,
+ * pblock_forward_variant, pblock_forward_train and pblock_backward record HIP
+ * events around each of their launches (or launch groups) on the call's stream;
+ * pblock_kernel_times then synchronises on the last recorded event and writes
+ * the summed milliseconds per category since the last reset into ms[0 .. n-1]
+ * (at most 9), in the order [layernorm, gemm_in, attention, gemm_out,
+ * bwd_transpose, bwd_gemm_dgrad, bwd_attention, bwd_gemm_wgrad, bwd_layernorm],
+ * plus the number of timed calls (the serial form's two LayerNorms count as
+ * layernorm, its QKV and FC1 GEMMs as gemm_in, its output-projection and FC2
+ * GEMMs as gemm_out).  Enabling or disabling resets the sums.  n must be >= 4. */
 int pblock_set_timing(pblock_t h, int enable);
 int pblock_kernel_times(pblock_t h, float* ms, int n, int* n_forwards);
 

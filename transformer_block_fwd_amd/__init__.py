@@ -19,6 +19,7 @@ from ._abi import (  # noqa: F401
     PBLOCK_F32,
     PblockCfg,
     PblockError,
+    PblockGrads,
     PblockVariant,
     PblockVariantWeights,
     PblockWeights,
@@ -30,9 +31,11 @@ __all__ = [
     "pblock_destroy", "pblock_intermediates", "pblock_copy_intermediates", "pblock_set_timing",
     "pblock_kernel_times", "pblock_swa_attention", "pblock_strerror", "pblock_last_error", "KERNEL_NAMES",
     "PblockVariant", "PblockVariantWeights", "make_variant", "pblock_forward_variant",
+    "PblockGrads", "pblock_train_workspace_bytes", "pblock_forward_train", "pblock_backward",
 ]
 
 KERNEL_NAMES = ("layernorm", "gemm_in", "attention", "gemm_out")
+BACKWARD_KERNEL_NAMES = ("bwd_transpose", "bwd_gemm_dgrad", "bwd_attention", "bwd_gemm_wgrad", "bwd_layernorm")
 
 _DTYPES = {"bf16": PBLOCK_BF16, "f32": PBLOCK_F32, PBLOCK_BF16: PBLOCK_BF16, PBLOCK_F32: PBLOCK_F32}
 
@@ -179,6 +182,50 @@ def pblock_forward_variant(handle: int, x, weights, extra, cfg, variant, out, st
                "pblock_forward_variant")
 
 
+def pblock_train_workspace_bytes(cfg) -> int:
+    c = as_cfg(cfg)
+    v = _abi.lib().pblock_train_workspace_bytes(ctypes.byref(c))
+    _abi.check(v if v < 0 else 0, "pblock_train_workspace_bytes")
+    return v
+
+
+def _check_weights(c, x, weights, extra=()):
+    gamma, beta, w_in, w_out = weights
+    M, A = c.B * c.S, c.H * c.hd
+    for t, name, n in ((x, "x", M * c.d), (gamma, "ln_gamma", c.d), (beta, "ln_beta", c.d),
+                       (w_in, "w_in", (3 * A + c.ffn) * c.d), (w_out, "w_out", c.d * (A + c.ffn))) + tuple(extra):
+        _check_tensor(t, name, c.dtype, n)
+    return PblockWeights(_ptr(gamma), _ptr(beta), _ptr(w_in), _ptr(w_out))
+
+
+def pblock_forward_train(handle: int, x, weights, cfg, out, ws, stream=None) -> None:
+    """pblock_forward plus the activations the backward needs, saved in ws (a device tensor of at
+    least pblock_train_workspace_bytes(cfg) bytes, 256-byte aligned)."""
+    c = as_cfg(cfg)
+    w = _check_weights(c, x, weights, ((out, "out", c.B * c.S * c.d),))
+    nbytes = ws.numel() * ws.element_size()
+    _abi.check(_abi.lib().pblock_forward_train(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), ctypes.byref(c),
+                                               _ptr(out), _ptr(ws), nbytes, _stream(stream)),
+               "pblock_forward_train")
+
+
+def pblock_backward(handle: int, x, weights, cfg, dy, grads, ws, stream=None) -> None:
+    """Gradients for dy of the forward saved in ws: grads = dict(dx, dln_gamma, dln_beta, dw_in, dw_out)
+    of device tensors shaped like x, ln_gamma, ln_beta, w_in, w_out."""
+    c = as_cfg(cfg)
+    M, A = c.B * c.S, c.H * c.hd
+    w = _check_weights(c, x, weights, (
+        (dy, "dy", M * c.d), (grads["dx"], "dx", M * c.d), (grads["dln_gamma"], "dln_gamma", c.d),
+        (grads["dln_beta"], "dln_beta", c.d), (grads["dw_in"], "dw_in", (3 * A + c.ffn) * c.d),
+        (grads["dw_out"], "dw_out", c.d * (A + c.ffn))))
+    g = PblockGrads(_ptr(grads["dx"]), _ptr(grads["dln_gamma"]), _ptr(grads["dln_beta"]), _ptr(grads["dw_in"]),
+                    _ptr(grads["dw_out"]))
+    nbytes = ws.numel() * ws.element_size()
+    _abi.check(_abi.lib().pblock_backward(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), ctypes.byref(c),
+                                          _ptr(dy), ctypes.byref(g), _ptr(ws), nbytes, _stream(stream)),
+               "pblock_backward")
+
+
 def _event_array(events, n, stream):
     """ctypes array of hipEvent_t handles for torch.cuda.Event objects (None entries stay NULL)."""
     if events is None:
@@ -238,13 +285,15 @@ def pblock_set_timing(handle: int, enable: bool) -> None:
     _abi.check(_abi.lib().pblock_set_timing(ctypes.c_void_p(handle), int(bool(enable))), "pblock_set_timing")
 
 
-def pblock_kernel_times(handle: int) -> tuple[dict, int]:
-    """Summed milliseconds per kernel since timing was enabled, and the forward count."""
-    ms = (ctypes.c_float * 4)()
+def pblock_kernel_times(handle: int, backward: bool = False) -> tuple[dict, int]:
+    """Summed milliseconds per kernel category since timing was enabled, and the number of
+    timed calls; the backward categories too with ``backward``."""
+    names = KERNEL_NAMES + (BACKWARD_KERNEL_NAMES if backward else ())
+    ms = (ctypes.c_float * len(names))()
     n = ctypes.c_int()
-    _abi.check(_abi.lib().pblock_kernel_times(ctypes.c_void_p(handle), ms, 4, ctypes.byref(n)),
+    _abi.check(_abi.lib().pblock_kernel_times(ctypes.c_void_p(handle), ms, len(names), ctypes.byref(n)),
                "pblock_kernel_times")
-    return dict(zip(KERNEL_NAMES, [float(v) for v in ms])), n.value
+    return dict(zip(names, [float(v) for v in ms])), n.value
 
 
 def pblock_swa_attention(qkv, ld_qkv, o, ld_o, B, S, H, hd, W, dtype="bf16", stream=None) -> None:

@@ -71,6 +71,16 @@ class PblockVariantWeights(ctypes.Structure):
     ]
 
 
+class PblockGrads(ctypes.Structure):
+    _fields_ = [
+        ("dx", ctypes.c_void_p),
+        ("dln_gamma", ctypes.c_void_p),
+        ("dln_beta", ctypes.c_void_p),
+        ("dw_in", ctypes.c_void_p),
+        ("dw_out", ctypes.c_void_p),
+    ]
+
+
 class PblockError(RuntimeError):
     def __init__(self, code: int, where: str, detail: str = ""):
         self.code = code
@@ -102,6 +112,11 @@ _SIGNATURES = {
     "pblock_forward_variant": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights),
                                           _c.POINTER(PblockVariantWeights), _c.POINTER(PblockCfg),
                                           _c.POINTER(PblockVariant), _c.c_void_p, _c.c_void_p]),
+    "pblock_train_workspace_bytes": (_c.c_int64, [_c.POINTER(PblockCfg)]),
+    "pblock_forward_train": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.POINTER(PblockCfg),
+                                        _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
+    "pblock_backward": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.POINTER(PblockCfg),
+                                   _c.c_void_p, _c.POINTER(PblockGrads), _c.c_void_p, _c.c_int64, _c.c_void_p]),
     "pblock_forward_chunked": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.POINTER(PblockCfg),
                                           _c.c_void_p, _c.c_int32, _c.POINTER(_c.c_void_p),
                                           _c.POINTER(_c.c_void_p), _c.c_void_p]),

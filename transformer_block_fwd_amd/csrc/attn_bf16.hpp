@@ -46,6 +46,8 @@ struct AttnArgs {
   int B, S, H, W;
   int q_lo, q_hi;       // query positions [q_lo, q_hi) of every sequence (0, S for all)
   float scale_log2;     // log2(e) / sqrt(hd)
+  float* lse;           // optional [B, H, S]: log2 of each query's softmax denominator in the
+                        // exponent's units, so that p_ij = 2^(s_ij * scale_log2 - lse) (backward pass)
 };
 
 constexpr int kAttnBQ = 128;
@@ -296,6 +298,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
 
   const float l = l_part + other_half(l_part);
   if (my_q < a.q_hi) {
+    if (a.lse != nullptr && lg == 0)
+      a.lse[(int64_t(b) * a.H + h) * S + my_q] = ((m_run == -INFINITY) ? 0.f : m_run) + log2f(l);
     const float inv = 1.0f / l;
     uint16_t* orow = a.o + (int64_t(b) * S + my_q) * a.ld_o + h * HD;
 #pragma unroll

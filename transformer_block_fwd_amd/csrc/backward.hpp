@@ -1,0 +1,221 @@
+// Elementwise and reduction kernels of the block's backward pass (bf16 storage, fp32 math):
+//   transpose_bf16_kernel   out[c, r] = in[r, c], zero-filled past the source rows, so that the
+//                           weight-gradient GEMMs (a contraction over tokens) see both operands
+//                           token-contiguous with the token count padded to the GEMM's k slab;
+//   layernorm_bwd_kernel    dx = (g - mean(g) - xhat mean(g xhat)) / sigma (+ dy), g = du gamma,
+//                           with per-workgroup column partials of du xhat and du;
+//   column_sum_kernel       dgamma, dbeta from those partials.
+// The chain rule through LayerNorm, GeLU and attention is the one the MegaScale guided reading's
+// section 3 implies for the backward pass ("the same is done in the backward pass").
+#pragma once
+
+#include "common.hpp"
+
+namespace pblk {
+
+// d/dz of z * Phi(z): Phi(z) + z * phi(z), with Phi from the same erfc approximation as
+// gelu_erf (Numerical Recipes erfcc, fractional error < 1.2e-7) and phi(z) = e^(-z^2/2)/sqrt(2 pi).
+__device__ __forceinline__ float gelu_erf_grad(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, x, 1.0f));
+  float p = 0.17087277f;
+  p = fmaf(t, p, -0.82215223f);
+  p = fmaf(t, p, 1.48851587f);
+  p = fmaf(t, p, -1.13520398f);
+  p = fmaf(t, p, 0.27886807f);
+  p = fmaf(t, p, -0.18628806f);
+  p = fmaf(t, p, 0.09678418f);
+  p = fmaf(t, p, 0.37409196f);
+  p = fmaf(t, p, 1.00002368f);
+  const float e = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);  // e^(-z^2/2)
+  const float h = 0.5f * t * e * __builtin_amdgcn_exp2f(fmaf(t, p, -1.26551223f) * 1.4426950408889634f);
+  const float Phi = z >= 0.0f ? 1.0f - h : h;
+  return fmaf(z * 0.3989422804014327f, e, Phi);
+}
+
+// 64 x 64 tiles through LDS; block 256 threads.  in [rows, cols] (row stride ld_in) ->
+// out [cols, out_cols] (row stride ld_out): out[c, r] = in[r, c] for r < rows, 0 for
+// rows <= r < out_cols.  cols and out_cols are multiples of 64, ld_in / ld_out of 8.
+// grid = (out_cols / 64) * (cols / 64).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t ld_in,
+                                                             int64_t rows, int64_t cols, uint16_t* __restrict__ out,
+                                                             int64_t ld_out, int64_t out_cols) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t tr = out_cols / 64;
+  const int64_t r0 = (blockIdx.x % tr) * 64, c0 = (blockIdx.x / tr) * 64;
+  const int tid = threadIdx.x;
+  // load: 64 rows x 64 columns = 512 pieces of 8; thread t takes pieces t and t + 256
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int piece = tid + 256 * p;
+    const int rr = piece >> 3, cc = (piece & 7) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + rr < rows) v = *reinterpret_cast<const u32x4*>(in + (r0 + rr) * ld_in + c0 + cc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[rr][cc + 2 * e] = uint16_t(v[e] & 0xFFFFu);
+      tile[rr][cc + 2 * e + 1] = uint16_t(v[e] >> 16);
+    }
+  }
+  __syncthreads();
+  // store: output row c0 + oc holds source column oc for source rows r0 .. r0+63
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int piece = tid + 256 * p;
+    const int oc = piece >> 3, orr = (piece & 7) * 8;
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = uint32_t(tile[orr + 2 * e][oc]) | (uint32_t(tile[orr + 2 * e + 1][oc]) << 16);
+    *reinterpret_cast<u32x4*>(out + (c0 + oc) * ld_out + r0 + orr) = v;
+  }
+}
+
+__device__ __forceinline__ float2 block_sum2_256(float a, float b, float* red) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();  // red[] may still be read from a previous reduction
+  if (lane == 0) {
+    red[wave] = a;
+    red[4 + wave] = b;
+  }
+  __syncthreads();
+  return make_float2(red[0] + red[1] + red[2] + red[3], red[4] + red[5] + red[6] + red[7]);
+}
+
+// One workgroup (256 threads) per `rows` consecutive rows of x [M, d] (bf16), du [M, d] (fp32),
+// dy [M, d] (bf16, may be null: no residual).  Writes dx [M, d] (bf16) and, per workgroup,
+// partial [blockIdx][0][d] = sum over its rows of du * xhat, partial [blockIdx][1][d] = sum du
+// (fp32).  VPT 8-element pieces per thread cover d (d <= VPT * 2048).
+template <int VPT>
+__global__ __launch_bounds__(256) void layernorm_bwd_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ gamma,
+                                                            const float* __restrict__ du,
+                                                            const uint16_t* __restrict__ dy,
+                                                            uint16_t* __restrict__ dx, float* __restrict__ partial,
+                                                            int64_t M, int d, int rows, float eps) {
+  __shared__ float red[8];
+  const int nvec = d / 8;
+  const int64_t row0 = int64_t(blockIdx.x) * rows;
+  const int64_t row_end = min(row0 + rows, M);
+  const float inv_d = 1.0f / float(d);
+  float pg[VPT][8], pb[VPT][8];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = 0.f;
+  for (int64_t row = row0; row < row_end; ++row) {
+    float xv[VPT][8];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * 256;
+      u32x4 r = {0u, 0u, 0u, 0u};
+      if (c < nvec) r = *reinterpret_cast<const u32x4*>(x + row * d + c * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[i][2 * e] = __uint_as_float(r[e] << 16);
+        xv[i][2 * e + 1] = __uint_as_float(r[e] & 0xFFFF0000u);
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += xv[i][e];
+    const float mean = block_sum2_256(s, 0.f, red).x * inv_d;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * 256;
+      if (c < nvec) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = xv[i][e] - mean;
+          q += t * t;
+        }
+      }
+    }
+    const float rstd = 1.0f / sqrtf(block_sum2_256(q, 0.f, red).x * inv_d + eps);
+    // g = du * gamma; sums of g and g * xhat
+    float gv[VPT][8];
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * 256;
+      if (c < nvec) {
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(du + row * d + c * 8);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(du + row * d + c * 8 + 4);
+        const u32x4 gr = *reinterpret_cast<const u32x4*>(gamma + c * 8);
+        const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float gm = (e & 1) ? __uint_as_float(gr[e >> 1] & 0xFFFF0000u) : __uint_as_float(gr[e >> 1] << 16);
+          const float xh = (xv[i][e] - mean) * rstd;
+          gv[i][e] = dv[e] * gm;
+          sg += gv[i][e];
+          sgx += gv[i][e] * xh;
+          pg[i][e] += dv[e] * xh;
+          pb[i][e] += dv[e];
+          xv[i][e] = xh;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[i][e] = 0.f;
+      }
+    }
+    const float2 sums = block_sum2_256(sg, sgx, red);
+    const float mg = sums.x * inv_d, mgx = sums.y * inv_d;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * 256;
+      if (c < nvec) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (gv[i][e] - mg - xv[i][e] * mgx) * rstd;
+        if (dy != nullptr) {
+          const u32x4 r = *reinterpret_cast<const u32x4*>(dy + row * d + c * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[2 * e] += __uint_as_float(r[e] << 16);
+            o[2 * e + 1] += __uint_as_float(r[e] & 0xFFFF0000u);
+          }
+        }
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 pr = {o[2 * e], o[2 * e + 1]};
+          w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        }
+        *reinterpret_cast<u32x4*>(dx + row * d + c * 8) = w;
+      }
+    }
+  }
+  float* pgo = partial + int64_t(blockIdx.x) * 2 * d;
+  float* pbo = pgo + d;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c = threadIdx.x + i * 256;
+    if (c < nvec) {
+      *reinterpret_cast<f32x4*>(pgo + c * 8) = f32x4{pg[i][0], pg[i][1], pg[i][2], pg[i][3]};
+      *reinterpret_cast<f32x4*>(pgo + c * 8 + 4) = f32x4{pg[i][4], pg[i][5], pg[i][6], pg[i][7]};
+      *reinterpret_cast<f32x4*>(pbo + c * 8) = f32x4{pb[i][0], pb[i][1], pb[i][2], pb[i][3]};
+      *reinterpret_cast<f32x4*>(pbo + c * 8 + 4) = f32x4{pb[i][4], pb[i][5], pb[i][6], pb[i][7]};
+    }
+  }
+}
+
+// out[j] = sum over p < n_part of partial[p][j], j < n (bf16 result).  One thread per column.
+__global__ __launch_bounds__(256) void column_sum_kernel(const float* __restrict__ partial, int n_part, int64_t n,
+                                                         uint16_t* __restrict__ out0, uint16_t* __restrict__ out1,
+                                                         int64_t half) {
+  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= n) return;
+  float s = 0.f;
+  for (int p = 0; p < n_part; ++p) s += partial[int64_t(p) * n + j];
+  const f32x2 pr = {s, 0.f};
+  const uint16_t v = uint16_t(__builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2)) & 0xFFFFu);
+  if (j < half) out0[j] = v;
+  else out1[j - half] = v;
+}
+
+}  // namespace pblk

@@ -20,7 +20,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 
 // GEMM epilogues (see gemm_bf16.hpp).
-enum { kEpiSplitGelu = 0, kEpiResidual = 1 };
+enum { kEpiSplitGelu = 0, kEpiResidual = 1, kEpiGeluBwd = 2, kEpiF32 = 3 };
 
 // bf16 values are stored as raw uint16 bits (the upper half of an fp32).
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }

@@ -53,12 +53,17 @@
 //     projections); columns >= nsplit get the exact GeLU and go to out1 at
 //     column off1 + (n - nsplit) (the FC1 activations next to the attention
 //     output, so the second GEMM reads one K-contiguous operand).
-//   kEpiResidual: optional residual x added in fp32, one rounding to bf16.
+//   kEpiResidual: optional residual x added in fp32, one rounding to bf16 (without it, a
+//     plain bf16 store).
+//   kEpiGeluBwd: columns < nsplit stored as bf16 to out0; columns >= nsplit multiplied by
+//     GeLU'(F) (F read from pre) and stored to out1 at column off1 + (n - nsplit).
+//   kEpiF32: fp32 store to out_f32 (row stride ld0).
 // Optional variant steps, in fp32 before the rounding: a bias per column (first), the
 // rotary embedding of the q and k columns, the tanh form of GeLU.
 // nsplit, the strides and off1 are multiples of 8.
 #pragma once
 
+#include "backward.hpp"
 #include "common.hpp"
 #include "rope.hpp"
 
@@ -85,6 +90,11 @@ struct GemmArgs {
   int seq;               // rows are sequences of seq positions (position = m % seq)
   int hd;
   int gelu_tanh;         // 1: tanh-form GeLU on the FC1 columns
+  // Backward-pass use: the FC1 pre-activation F [M, N - nsplit] (row stride ld_pre), stored by
+  // kEpiSplitGelu when non-null and read by kEpiGeluBwd; fp32 output of kEpiF32.
+  uint16_t* pre;
+  int64_t ld_pre;
+  float* out_f32;
 };
 
 constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 64, kGemmThreads = 256;
@@ -148,6 +158,11 @@ __device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f3
       if (n < g.rope_n) rope_rotate8(v, g.rope, m % g.seq, n & (g.hd - 1), g.hd);
       dst = g.out0 + int64_t(m) * g.ld0 + n;
     } else {
+      if (g.pre != nullptr) {
+        const u32x4 pw = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7])};
+        *reinterpret_cast<u32x4*>(g.pre + int64_t(m) * g.ld_pre + (n - g.nsplit)) = pw;
+      }
       if (g.gelu_tanh) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = gelu_tanh(v[e]);
@@ -157,6 +172,23 @@ __device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f3
       }
       dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
     }
+  } else if constexpr (EPI == kEpiGeluBwd) {
+    if (n < g.nsplit) {
+      dst = g.out0 + int64_t(m) * g.ld0 + n;
+    } else {
+      const u32x4 fr = *reinterpret_cast<const u32x4*>(g.pre + int64_t(m) * g.ld_pre + (n - g.nsplit));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] *= gelu_erf_grad(__uint_as_float(fr[e] << 16));
+        v[2 * e + 1] *= gelu_erf_grad(__uint_as_float(fr[e] & 0xFFFF0000u));
+      }
+      dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
+    }
+  } else if constexpr (EPI == kEpiF32) {
+    f32x4* o = reinterpret_cast<f32x4*>(g.out_f32 + int64_t(m) * g.ld0 + n);
+    o[0] = f32x4{v[0], v[1], v[2], v[3]};
+    o[1] = f32x4{v[4], v[5], v[6], v[7]};
+    return;
   } else {
     if (g.resid != nullptr) {
       const u32x4 xr = *reinterpret_cast<const u32x4*>(g.resid + int64_t(m) * g.ldr + n);

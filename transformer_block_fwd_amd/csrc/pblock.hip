@@ -22,7 +22,9 @@
 
 #include "../../include/pblock.h"
 #include "attn_bf16.hpp"
+#include "attn_bwd_bf16.hpp"
 #include "attn_f32.hpp"
+#include "backward.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
 #include "layernorm.hpp"
@@ -248,11 +250,12 @@ void launch_gemm_f32(const GemmArgsF32& g, hipStream_t s) {
 
 // Attention for query positions [q_lo, q_hi) of each of the B sequences.
 void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, int B, int S, int H, int hd, int W,
-                      int dtype, hipStream_t s, int q_lo = 0, int q_hi = -1) {
+                      int dtype, hipStream_t s, int q_lo = 0, int q_hi = -1, float* lse = nullptr) {
   if (q_hi < 0) q_hi = S;
   const float scale = 1.0f / std::sqrt(float(hd));
   if (dtype == PBLOCK_BF16) {
-    AttnArgs a;
+    AttnArgs a{};
+    a.lse = lse;
     a.qkv = static_cast<const uint16_t*>(qkv);
     a.ld_qkv = ld_qkv;
     a.o = static_cast<uint16_t*>(o);
@@ -274,8 +277,10 @@ void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, in
   }
 }
 
-constexpr int kTimedKernels = 4;  // categories: layernorm, gemm_in, attention, gemm_out
-constexpr int kMaxLaunches = 8;   // launches of one forward that get their own event pair
+// timing categories: layernorm, gemm_in, attention, gemm_out (forward); transpose,
+// gemm_dgrad, attention, gemm_wgrad, layernorm (backward)
+constexpr int kTimedKernels = 9;
+constexpr int kMaxLaunches = 12;  // launches (or launch groups) of one call that get their own event pair
 constexpr size_t kEventPool = 256;
 
 // Events of one timed forward: ev[k] .. ev[k+1] brackets launch k, of category cat[k].
@@ -415,6 +420,8 @@ struct InEpi {
   int seq = 1;  // positions per sequence: row m is at position m % seq
   int hd = 64;
   int gelu_tanh = 0;
+  void* pre = nullptr;  // FC1 pre-activation store [M, N - nsplit] (row stride ld_pre), bf16 only
+  int64_t ld_pre = 0;
 };
 
 // out0[m, n] = Z[m, n] for n < nsplit; out1[m, off1 + n - nsplit] = GeLU(Z[m, n]) otherwise;
@@ -433,6 +440,8 @@ void run_gemm_in(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t
     g.bias = static_cast<const uint16_t*>(ep.bias);
     g.rope = ep.rope; g.rope_n = ep.rope_n; g.seq = ep.seq; g.hd = ep.hd;
     g.gelu_tanh = ep.gelu_tanh;
+    g.pre = static_cast<uint16_t*>(ep.pre);
+    g.ld_pre = ep.ld_pre;
     launch_gemm_bf16<kEpiSplitGelu>(g, scr, s);
   } else {
     GemmArgsF32 g{};
@@ -472,6 +481,82 @@ void run_gemm_out(const void* a, int64_t lda, const void* b, int64_t ldb, int64_
     g.bias = static_cast<const float*>(bias);
     launch_gemm_f32<kEpiResidual>(g, s);
   }
+}
+
+// ------------------------------------------------------------------------ training
+
+// Caller-owned training workspace: the activations pblock_forward_train saves (u, q|k|v,
+// [attention | GeLU], the FC1 pre-activation F, the softmax log-sum-exp) and the backward
+// pass's scratch.  Offsets depend on the call's B*S, so forward_train and backward must be
+// called with the same cfg.
+struct TrainLayout {
+  int64_t u, qkv, ag, f, lse, delta, dyp, dO, dz, du, woT, wiT, dyT, agT, dzT, uT, part, total;
+  int64_t Mp, ln_rows, ln_grid;
+};
+TrainLayout train_layout(const pblock_cfg* c) {
+  const Dims dm = dims(c);
+  const int64_t es = 2, M = dm.M, d = c->d;
+  const int64_t m256 = (M + kGemmBM - 1) / kGemmBM * kGemmBM;
+  const int64_t Mt = m256 + kGemmBM;
+  TrainLayout t;
+  t.Mp = (M + kGemmBK - 1) / kGemmBK * kGemmBK;  // token count padded to the GEMM's k slab
+  t.ln_rows = std::max<int64_t>(1, (M + 255) / 256);
+  t.ln_grid = (M + t.ln_rows - 1) / t.ln_rows;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  t.u = take(Mt * d * es);  // GEMM row operands: whole 256-row tiles (+ one, as the forward's)
+  t.qkv = take(M * 3 * dm.A * es);
+  t.ag = take(Mt * dm.k_out * es);
+  t.f = take(M * c->ffn * es);
+  t.lse = take(M * c->H * 4);
+  t.delta = take(M * c->H * 4);
+  t.dyp = take(m256 * d * es);
+  t.dO = take(M * dm.A * es);
+  t.dz = take(m256 * dm.n_in * es);
+  t.du = take(M * d * 4);
+  t.woT = take(dm.k_out * d * es);
+  t.wiT = take(d * dm.n_in * es);
+  t.dyT = take((d + kGemmBM - 1) / kGemmBM * kGemmBM * t.Mp * es);
+  t.agT = take(dm.k_out * t.Mp * es);
+  t.dzT = take((dm.n_in + kGemmBM - 1) / kGemmBM * kGemmBM * t.Mp * es);
+  t.uT = take(d * t.Mp * es);
+  t.part = take(t.ln_grid * 2 * d * 4);
+  t.total = o;
+  return t;
+}
+
+// out [cols, out_cols] = in [rows, cols]^T, zero past `rows` (bf16).
+void launch_transpose(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out, int64_t ld_out,
+                      int64_t out_cols, hipStream_t s) {
+  const unsigned grid = unsigned((out_cols / 64) * (cols / 64));
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(grid), dim3(256), 0, s, static_cast<const uint16_t*>(in), ld_in,
+                     rows, cols, static_cast<uint16_t*>(out), ld_out, out_cols);
+}
+
+constexpr int kBwdMaxD = 16384;  // LayerNorm backward holds up to 8 vectors of 8 per thread
+
+int check_train(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* ws, int64_t ws_bytes,
+                Dims* dm, TrainLayout* lay) {
+  if (!ws) return fail(PBLOCK_ERR_NULL, "training workspace is NULL");
+  // the shared checks, with the workspace in the place of out (the real out is checked by the caller)
+  int st = check_forward(h, x, w, cfg, ws, dm);
+  if (st != PBLOCK_OK) return st;
+  if (cfg->dtype != PBLOCK_BF16) return fail(PBLOCK_ERR_DTYPE, "the training path is bf16 only");
+  if (cfg->d > kBwdMaxD) return fail(PBLOCK_ERR_SHAPE, "the backward pass supports d <= 16384");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(PBLOCK_ERR_ALIGN, "training workspace must be 256-byte aligned");
+  *lay = train_layout(cfg);
+  if (ws_bytes < lay->total) return fail(PBLOCK_ERR_ARG, "training workspace too small (pblock_train_workspace_bytes)");
+  const int64_t es = 2;
+  const int64_t xb = dm->M * cfg->d * es;
+  if (overlap(ws, lay->total, x, xb) || overlap(ws, lay->total, w->w_in, dm->n_in * cfg->d * es) ||
+      overlap(ws, lay->total, w->w_out, int64_t(cfg->d) * dm->k_out * es) ||
+      overlap(ws, lay->total, w->ln_gamma, cfg->d * es) || overlap(ws, lay->total, w->ln_beta, cfg->d * es))
+    return fail(PBLOCK_ERR_ALIAS, "training workspace overlaps x or a weight");
+  return PBLOCK_OK;
 }
 
 }  // namespace
@@ -601,10 +686,10 @@ int pblock_set_timing(pblock_t h, int enable) {
 
 int pblock_kernel_times(pblock_t h, float* ms, int n, int* n_forwards) {
   if (!h || !ms) return fail(PBLOCK_ERR_NULL, "handle or ms is NULL");
-  if (n < kTimedKernels) return fail(PBLOCK_ERR_ARG, "n must be >= 4");
+  if (n < 4) return fail(PBLOCK_ERR_ARG, "n must be >= 4");
   int st = drain_events(h);
   if (st != PBLOCK_OK) return st;
-  for (int k = 0; k < kTimedKernels; ++k) ms[k] = float(h->ms_sum[k]);
+  for (int k = 0; k < std::min(n, kTimedKernels); ++k) ms[k] = float(h->ms_sum[k]);
   if (n_forwards) *n_forwards = h->n_forwards;
   return PBLOCK_OK;
 }
@@ -819,6 +904,181 @@ int pblock_forward_variant(pblock_t h, const void* x, const pblock_weights* w, c
     tm.mark(3);
     h->last_m = dm.M;
     return launch_status("pblock_forward_variant launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int64_t pblock_train_workspace_bytes(const pblock_cfg* cfg) {
+  const int st = validate(cfg);
+  if (st != PBLOCK_OK) return st;
+  if (cfg->dtype != PBLOCK_BF16) return fail(PBLOCK_ERR_DTYPE, "the training path is bf16 only");
+  if (cfg->d > kBwdMaxD) return fail(PBLOCK_ERR_SHAPE, "the backward pass supports d <= 16384");
+  return train_layout(cfg).total;
+}
+
+int pblock_forward_train(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out,
+                         void* ws, int64_t ws_bytes, void* stream) {
+  try {
+    Dims dm;
+    TrainLayout T;
+    int st = check_train(h, x, w, cfg, ws, ws_bytes, &dm, &T);
+    if (st != PBLOCK_OK) return st;
+    st = check_forward(h, x, w, cfg, out, &dm);
+    if (st != PBLOCK_OK) return st;
+    const pblock_cfg& c = *cfg;
+    if (overlap(out, dm.M * c.d * 2, ws, T.total)) return fail(PBLOCK_ERR_ALIAS, "out overlaps the training workspace");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(ws);
+    const Ws hw = workspace(h);
+    const int64_t A = dm.A;
+    Timer tm;
+    st = tm.begin(h, s);
+    if (st != PBLOCK_OK) return st;
+    run_layernorm(x, w->ln_gamma, w->ln_beta, base + T.u, dm.M, c, s);
+    tm.mark(0);
+    InEpi ep;
+    ep.pre = base + T.f;
+    ep.ld_pre = c.ffn;
+    run_gemm_in(base + T.u, c.d, w->w_in, c.d, dm.M, dm.n_in, c.d, base + T.qkv, 3 * A, base + T.ag, dm.k_out, A, 3 * A,
+                c.dtype, hw.scr, s, ep);
+    tm.mark(1);
+    launch_attention(base + T.qkv, 3 * A, base + T.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s, 0, -1,
+                     reinterpret_cast<float*>(base + T.lse));
+    tm.mark(2);
+    run_gemm_out(base + T.ag, dm.k_out, w->w_out, dm.k_out, dm.M, c.d, dm.k_out, out, c.add_residual ? x : nullptr,
+                 c.dtype, hw.scr, s);
+    tm.mark(3);
+    h->last_m = dm.M;
+    return launch_status("pblock_forward_train launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, const void* dy,
+                    const pblock_grads* grads, void* ws, int64_t ws_bytes, void* stream) {
+  try {
+    Dims dm;
+    TrainLayout T;
+    int st = check_train(h, x, w, cfg, ws, ws_bytes, &dm, &T);
+    if (st != PBLOCK_OK) return st;
+    const pblock_cfg& c = *cfg;
+    if (!dy || !grads || !grads->dx || !grads->dln_gamma || !grads->dln_beta || !grads->dw_in || !grads->dw_out)
+      return fail(PBLOCK_ERR_NULL, "dy, grads or a gradient pointer is NULL");
+    const int64_t es = 2, A = dm.A, M = dm.M, d = c.d;
+    const struct { const void* p; int64_t bytes; } outs[5] = {
+        {grads->dx, M * d * es}, {grads->dln_gamma, d * es}, {grads->dln_beta, d * es},
+        {grads->dw_in, dm.n_in * d * es}, {grads->dw_out, d * dm.k_out * es}};
+    const struct { const void* p; int64_t bytes; } ins[7] = {
+        {x, M * d * es}, {dy, M * d * es}, {w->w_in, dm.n_in * d * es}, {w->w_out, d * dm.k_out * es},
+        {w->ln_gamma, d * es}, {w->ln_beta, d * es}, {ws, T.total}};
+    if (!aligned16(dy)) return fail(PBLOCK_ERR_ALIGN, "dy must be 16-byte aligned");
+    for (int i = 0; i < 5; ++i) {
+      if (!aligned16(outs[i].p)) return fail(PBLOCK_ERR_ALIGN, "gradient pointers must be 16-byte aligned");
+      for (const auto& in : ins)
+        if (overlap(outs[i].p, outs[i].bytes, in.p, in.bytes))
+          return fail(PBLOCK_ERR_ALIAS, "a gradient overlaps an input, a weight or the workspace");
+      for (int j = 0; j < i; ++j)
+        if (overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+          return fail(PBLOCK_ERR_ALIAS, "gradients overlap each other");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(ws);
+    const Ws hw = workspace(h);
+    Timer tm;
+    st = tm.begin(h, s);
+    if (st != PBLOCK_OK) return st;
+
+    // dy into whole 256-row tiles (the GEMM's row operand), W_out^T and W_in^T (K-contiguous
+    // second operands of the two activation-gradient GEMMs)
+    hipError_t e = hipMemcpyAsync(base + T.dyp, dy, size_t(M * d * es), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
+    launch_transpose(w->w_out, dm.k_out, d, dm.k_out, base + T.woT, d, d, s);
+    launch_transpose(w->w_in, d, dm.n_in, d, base + T.wiT, dm.n_in, dm.n_in, s);
+    tm.mark(4);
+    // [dO | dG] = dy W_out; dF = dG * GeLU'(F) straight into dz's FC1 columns
+    {
+      GemmArgs g{};
+      g.a = reinterpret_cast<const uint16_t*>(base + T.dyp); g.lda = d;
+      g.b = reinterpret_cast<const uint16_t*>(base + T.woT); g.ldb = d;
+      g.M = int(M); g.N = int(dm.k_out); g.K = int(d);
+      g.out0 = reinterpret_cast<uint16_t*>(base + T.dO); g.ld0 = A;
+      g.out1 = reinterpret_cast<uint16_t*>(base + T.dz); g.ld1 = dm.n_in; g.off1 = 3 * A;
+      g.nsplit = int(A);
+      g.pre = reinterpret_cast<uint16_t*>(base + T.f); g.ld_pre = c.ffn;
+      launch_gemm_bf16<kEpiGeluBwd>(g, hw.scr, s);
+    }
+    tm.mark(5);
+    // attention backward: dQ (and D), then dK, dV, into dz's Q|K|V columns
+    {
+      AttnBwdArgs ab{};
+      ab.qkv = reinterpret_cast<const uint16_t*>(base + T.qkv); ab.ld_qkv = 3 * A;
+      ab.o = reinterpret_cast<const uint16_t*>(base + T.ag); ab.ld_o = dm.k_out;
+      ab.dout = reinterpret_cast<const uint16_t*>(base + T.dO); ab.ld_do = A;
+      ab.lse = reinterpret_cast<const float*>(base + T.lse);
+      ab.delta = reinterpret_cast<float*>(base + T.delta);
+      ab.dqkv = reinterpret_cast<uint16_t*>(base + T.dz); ab.ld_dqkv = dm.n_in;
+      ab.B = c.B; ab.S = c.S; ab.H = c.H; ab.W = c.W;
+      ab.scale = 1.0f / std::sqrt(float(c.hd));
+      ab.scale_log2 = ab.scale * 1.4426950408889634f;
+      const unsigned gq = unsigned(int64_t((c.S + kAttnBQ - 1) / kAttnBQ) * c.B * c.H);
+      const unsigned gk = unsigned(int64_t((c.S + 127) / 128) * c.B * c.H);
+      if (c.hd == 128) {
+        hipLaunchKernelGGL((swa_attn_bwd_dq_kernel<128>), dim3(gq), dim3(kAttnThreads), 0, s, ab);
+        hipLaunchKernelGGL((swa_attn_bwd_dkdv_kernel<128>), dim3(gk), dim3(kAttnThreads), 0, s, ab);
+      } else {
+        hipLaunchKernelGGL((swa_attn_bwd_dq_kernel<64>), dim3(gq), dim3(kAttnThreads), 0, s, ab);
+        hipLaunchKernelGGL((swa_attn_bwd_dkdv_kernel<64>), dim3(gk), dim3(kAttnThreads), 0, s, ab);
+      }
+    }
+    tm.mark(6);
+    // du = dz W_in (fp32)
+    {
+      GemmArgs g{};
+      g.a = reinterpret_cast<const uint16_t*>(base + T.dz); g.lda = dm.n_in;
+      g.b = reinterpret_cast<const uint16_t*>(base + T.wiT); g.ldb = dm.n_in;
+      g.M = int(M); g.N = int(d); g.K = int(dm.n_in);
+      g.ld0 = d;
+      g.out_f32 = reinterpret_cast<float*>(base + T.du);
+      launch_gemm_bf16<kEpiF32>(g, hw.scr, s);
+    }
+    tm.mark(5);
+    // LayerNorm backward (+ dy for the residual), dgamma and dbeta
+    {
+      const int need = int((d / 8 + 255) / 256);
+      const dim3 grid{unsigned(T.ln_grid)}, block{256};
+      const auto* xp = static_cast<const uint16_t*>(x);
+      const auto* gp = static_cast<const uint16_t*>(w->ln_gamma);
+      const auto* dup = reinterpret_cast<const float*>(base + T.du);
+      const auto* dyr = c.add_residual ? static_cast<const uint16_t*>(dy) : nullptr;
+      auto* dxp = static_cast<uint16_t*>(grads->dx);
+      auto* part = reinterpret_cast<float*>(base + T.part);
+      const int rows = int(T.ln_rows);
+#define PBLK_LNB(V) hipLaunchKernelGGL((layernorm_bwd_kernel<V>), grid, block, 0, s, xp, gp, dup, dyr, dxp, part, M, int(d), rows, c.ln_eps)
+      if (need <= 1) PBLK_LNB(1);
+      else if (need <= 2) PBLK_LNB(2);
+      else if (need <= 3) PBLK_LNB(3);
+      else if (need <= 4) PBLK_LNB(4);
+      else if (need <= 6) PBLK_LNB(6);
+      else PBLK_LNB(8);
+#undef PBLK_LNB
+      hipLaunchKernelGGL(column_sum_kernel, dim3(unsigned((2 * d + 255) / 256)), dim3(256), 0, s, part,
+                         int(T.ln_grid), 2 * d, static_cast<uint16_t*>(grads->dln_gamma),
+                         static_cast<uint16_t*>(grads->dln_beta), d);
+    }
+    tm.mark(8);
+    // token-contiguous operands of the weight-gradient GEMMs (token count padded with zeros)
+    launch_transpose(dy, d, M, d, base + T.dyT, T.Mp, T.Mp, s);
+    launch_transpose(base + T.ag, dm.k_out, M, dm.k_out, base + T.agT, T.Mp, T.Mp, s);
+    launch_transpose(base + T.dz, dm.n_in, M, dm.n_in, base + T.dzT, T.Mp, T.Mp, s);
+    launch_transpose(base + T.u, d, M, d, base + T.uT, T.Mp, T.Mp, s);
+    tm.mark(4);
+    // dW_out = dy^T [A | G], dW_in = dz^T u
+    run_gemm_out(base + T.dyT, T.Mp, base + T.agT, T.Mp, d, dm.k_out, T.Mp, grads->dw_out, nullptr, c.dtype, hw.scr, s);
+    run_gemm_out(base + T.dzT, T.Mp, base + T.uT, T.Mp, dm.n_in, d, T.Mp, grads->dw_in, nullptr, c.dtype, hw.scr, s);
+    tm.mark(7);
+    return launch_status("pblock_backward launch");
   } catch (...) {
     return fail(PBLOCK_ERR_ARG, "internal error");
   }

@@ -210,6 +210,17 @@ def make_variant_params(cfg: BlockConfig, seed: int = 0) -> dict[str, np.ndarray
     return dict(b_in=b_in, b_out=b_out, b_in_dev=b_in, b_out_dev=b_out)
 
 
+def make_dy(cfg: BlockConfig, seed: int = 0) -> dict[str, np.ndarray]:
+    """Output gradient dy [B, S, d] ~ N(0, 1) for the backward pass, from its own stream;
+    float32 values as the device receives them under "dy" and the storage array under "dy_dev"."""
+    rng = np.random.Generator(np.random.PCG64([seed, 4]))
+    dy = rng.standard_normal((cfg.B, cfg.S, cfg.d), dtype=np.float32)
+    if cfg.dtype == "bf16":
+        v, bits = round_to_bf16(dy)
+        return dict(dy=v, dy_dev=bits)
+    return dict(dy=dy, dy_dev=dy)
+
+
 def sample_row_blocks(cfg: BlockConfig, block: int = 32, seed: int = 1) -> list[tuple[int, int, int]]:
     """Query row blocks (b, i0, i1) for sampled checks at full size.
 
