@@ -143,3 +143,20 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not found"):
         tb.pblock_validate_cfg(CONFIGS["tiny"])
+
+
+def test_train_workspace_bytes():
+    """The training workspace is sized on the host: bf16 only, d <= 16384, and at least the saved
+    activations (u, q|k|v, [attention | GeLU], FC1 pre-activation) plus the transposed weights."""
+    for name, cfg in CONFIGS.items():
+        if cfg.dtype != "bf16":
+            with pytest.raises(tb.PblockError) as ei:
+                tb.pblock_train_workspace_bytes(cfg)
+            assert ei.value.code == _abi.PBLOCK_ERR_DTYPE
+            continue
+        n = tb.pblock_train_workspace_bytes(cfg)
+        floor = 2 * (cfg.M * (cfg.d + 3 * cfg.A + cfg.k_out + cfg.ffn) + 2 * cfg.d * cfg.n_in)
+        assert n >= floor, name
+    big = tb.as_cfg(CONFIGS["small"])
+    big.d = 16384 + 64
+    assert _abi.lib().pblock_train_workspace_bytes(ctypes.byref(big)) == _abi.PBLOCK_ERR_SHAPE

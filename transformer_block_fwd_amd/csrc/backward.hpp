@@ -3,7 +3,8 @@
 //                           weight-gradient GEMMs (a contraction over tokens) see both operands
 //                           token-contiguous with the token count padded to the GEMM's k slab;
 //   layernorm_bwd_kernel    dx = (g - mean(g) - xhat mean(g xhat)) / sigma (+ dy), g = du gamma,
-//                           with per-workgroup column partials of du xhat and du;
+//                           from the forward's per-row mean and 1/sigma, with per-workgroup
+//                           column partials of du xhat and du;
 //   column_sum_kernel       dgamma, dbeta from those partials.
 // The chain rule through LayerNorm, GeLU and attention is the one the MegaScale guided reading's
 // section 3 implies for the backward pass ("the same is done in the backward pass").
@@ -84,16 +85,18 @@ __device__ __forceinline__ float2 block_sum2_256(float a, float b, float* red) {
 }
 
 // One workgroup (256 threads) per `rows` consecutive rows of x [M, d] (bf16), du [M, d] (fp32),
-// dy [M, d] (bf16, may be null: no residual).  Writes dx [M, d] (bf16) and, per workgroup,
-// partial [blockIdx][0][d] = sum over its rows of du * xhat, partial [blockIdx][1][d] = sum du
-// (fp32).  VPT 8-element pieces per thread cover d (d <= VPT * 2048).
+// dy [M, d] (bf16, may be null: no residual), with each row's mean and 1/sigma from the forward
+// (stats [M][2]).  Writes dx [M, d] (bf16) and, per workgroup, partial [blockIdx][0][d] = sum over
+// its rows of du * xhat, partial [blockIdx][1][d] = sum du (fp32).  VPT 8-element pieces per
+// thread cover d (d <= VPT * 2048).  One block reduction per row (sum g, sum g * xhat).
 template <int VPT>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ gamma,
                                                             const float* __restrict__ du,
                                                             const uint16_t* __restrict__ dy,
+                                                            const float* __restrict__ stats,
                                                             uint16_t* __restrict__ dx, float* __restrict__ partial,
-                                                            int64_t M, int d, int rows, float eps) {
+                                                            int64_t M, int d, int rows) {
   __shared__ float red[8];
   const int nvec = d / 8;
   const int64_t row0 = int64_t(blockIdx.x) * rows;
@@ -105,62 +108,31 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(const uint16_t* __re
 #pragma unroll
     for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = 0.f;
   for (int64_t row = row0; row < row_end; ++row) {
-    float xv[VPT][8];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = threadIdx.x + i * 256;
-      u32x4 r = {0u, 0u, 0u, 0u};
-      if (c < nvec) r = *reinterpret_cast<const u32x4*>(x + row * d + c * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xv[i][2 * e] = __uint_as_float(r[e] << 16);
-        xv[i][2 * e + 1] = __uint_as_float(r[e] & 0xFFFF0000u);
-      }
-    }
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += xv[i][e];
-    const float mean = block_sum2_256(s, 0.f, red).x * inv_d;
-    float q = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = threadIdx.x + i * 256;
-      if (c < nvec) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float t = xv[i][e] - mean;
-          q += t * t;
-        }
-      }
-    }
-    const float rstd = 1.0f / sqrtf(block_sum2_256(q, 0.f, red).x * inv_d + eps);
-    // g = du * gamma; sums of g and g * xhat
-    float gv[VPT][8];
+    const float mean = stats[2 * row], rstd = stats[2 * row + 1];
+    // xhat and g = du * gamma; sums of g and g * xhat
+    float xh[VPT][8], gv[VPT][8];
     float sg = 0.f, sgx = 0.f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = threadIdx.x + i * 256;
       if (c < nvec) {
+        const u32x4 xr = *reinterpret_cast<const u32x4*>(x + row * d + c * 8);
         const f32x4 d0 = *reinterpret_cast<const f32x4*>(du + row * d + c * 8);
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(du + row * d + c * 8 + 4);
         const u32x4 gr = *reinterpret_cast<const u32x4*>(gamma + c * 8);
         const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float gm = (e & 1) ? __uint_as_float(gr[e >> 1] & 0xFFFF0000u) : __uint_as_float(gr[e >> 1] << 16);
-          const float xh = (xv[i][e] - mean) * rstd;
+          const uint32_t xw = xr[e >> 1], gw = gr[e >> 1];
+          const float xe = (e & 1) ? __uint_as_float(xw & 0xFFFF0000u) : __uint_as_float(xw << 16);
+          const float gm = (e & 1) ? __uint_as_float(gw & 0xFFFF0000u) : __uint_as_float(gw << 16);
+          xh[i][e] = (xe - mean) * rstd;
           gv[i][e] = dv[e] * gm;
           sg += gv[i][e];
-          sgx += gv[i][e] * xh;
-          pg[i][e] += dv[e] * xh;
+          sgx += gv[i][e] * xh[i][e];
+          pg[i][e] += dv[e] * xh[i][e];
           pb[i][e] += dv[e];
-          xv[i][e] = xh;
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gv[i][e] = 0.f;
       }
     }
     const float2 sums = block_sum2_256(sg, sgx, red);
@@ -171,7 +143,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(const uint16_t* __re
       if (c < nvec) {
         float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (gv[i][e] - mg - xv[i][e] * mgx) * rstd;
+        for (int e = 0; e < 8; ++e) o[e] = (gv[i][e] - mg - xh[i][e] * mgx) * rstd;
         if (dy != nullptr) {
           const u32x4 r = *reinterpret_cast<const u32x4*>(dy + row * d + c * 8);
 #pragma unroll
@@ -204,18 +176,26 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(const uint16_t* __re
   }
 }
 
-// out[j] = sum over p < n_part of partial[p][j], j < n (bf16 result).  One thread per column.
+// out[j] = sum over p < n_part of partial[p][j] for the 64 columns j of this workgroup (n a
+// multiple of 64): thread (g, c) sums the rows p = g mod 4 of column c, then the four partial
+// sums meet in LDS in a fixed order (bf16 result: j < half to out0, else out1).
 __global__ __launch_bounds__(256) void column_sum_kernel(const float* __restrict__ partial, int n_part, int64_t n,
                                                          uint16_t* __restrict__ out0, uint16_t* __restrict__ out1,
                                                          int64_t half) {
-  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (j >= n) return;
+  __shared__ float red[4][64];
+  const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int64_t j = int64_t(blockIdx.x) * 64 + c;
   float s = 0.f;
-  for (int p = 0; p < n_part; ++p) s += partial[int64_t(p) * n + j];
-  const f32x2 pr = {s, 0.f};
-  const uint16_t v = uint16_t(__builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2)) & 0xFFFFu);
-  if (j < half) out0[j] = v;
-  else out1[j - half] = v;
+  for (int p = g; p < n_part; p += 4) s += partial[int64_t(p) * n + j];
+  red[g][c] = s;
+  __syncthreads();
+  if (g == 0) {
+    const float t = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    const f32x2 pr = {t, 0.f};
+    const uint16_t v = uint16_t(__builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2)) & 0xFFFFu);
+    if (j < half) out0[j] = v;
+    else out1[j - half] = v;
+  }
 }
 
 }  // namespace pblk

@@ -67,14 +67,16 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 }
 
 // VPT = 16-byte vectors per thread (the host picks the smallest that covers d).  Each
-// workgroup normalizes rows_per_wg consecutive rows.  For rows of up to 2048 vectors
+// workgroup normalizes rows_per_wg consecutive rows; `stats` (optional, [M][2]) receives each
+// row's mean and 1/sigma.  For rows of up to 2048 vectors
 // (VPT <= 8) gamma and beta stay in registers across the rows and the next row's loads
 // are in flight while the current one is reduced and written; wider rows take one row
 // per workgroup (the host passes rows_per_wg = 1) and read gamma and beta per row.
 template <typename T, int VPT>
 __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
                                                                const T* __restrict__ beta, T* __restrict__ u,
-                                                               int64_t M, int d, int rows_per_wg, float eps) {
+                                                               int64_t M, int d, int rows_per_wg, float eps,
+                                                               float* __restrict__ stats) {
   using V = LnVec<T>;
   using Raw = typename V::Raw;
   constexpr int N = V::N;
@@ -131,6 +133,10 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restri
     }
     const float var = block_sum_256(q, red) * inv_d;
     const float rstd = 1.0f / sqrtf(var + eps);
+    if (stats != nullptr && threadIdx.x == 0) {  // mean and 1/sigma of the row, for the backward pass
+      stats[2 * row] = mean;
+      stats[2 * row + 1] = rstd;
+    }
     T* ur = u + row * d;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {

@@ -181,7 +181,8 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(int iters, float* sin
 // ------------------------------------------------------------------------ launches
 
 template <typename T>
-void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d, float eps, hipStream_t s) {
+void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d, float eps, hipStream_t s,
+                      float* stats = nullptr) {
   const int per = 16 / int(sizeof(T));
   const int need = (d / per + kLnThreads - 1) / kLnThreads;
   // Rows per workgroup: wide rows (>= 16 KiB) gain from gamma/beta reuse and the next-row
@@ -191,7 +192,7 @@ void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d
   const int want = row_bytes >= 16384 ? kLnMaxRows : (row_bytes >= 4096 ? 2 : 1);
   const int rows = need > 8 ? 1 : int(std::max<int64_t>(1, std::min<int64_t>(want, M / 512)));
   const dim3 grid{static_cast<unsigned>((M + rows - 1) / rows)}, block{kLnThreads};
-#define PBLK_LN(V) hipLaunchKernelGGL((layernorm_kernel<T, V>), grid, block, 0, s, x, g, b, u, M, d, rows, eps)
+#define PBLK_LN(V) hipLaunchKernelGGL((layernorm_kernel<T, V>), grid, block, 0, s, x, g, b, u, M, d, rows, eps, stats)
   if (need <= 1) PBLK_LN(1);
   else if (need <= 2) PBLK_LN(2);
   else if (need <= 3) PBLK_LN(3);
@@ -403,10 +404,11 @@ struct Timer {
   }
 };
 
-void run_layernorm(const void* x, const void* g, const void* b, void* u, int64_t M, const pblock_cfg& c, hipStream_t s) {
+void run_layernorm(const void* x, const void* g, const void* b, void* u, int64_t M, const pblock_cfg& c, hipStream_t s,
+                   float* stats = nullptr) {
   if (c.dtype == PBLOCK_BF16)
     launch_layernorm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(b),
-                     static_cast<uint16_t*>(u), M, c.d, c.ln_eps, s);
+                     static_cast<uint16_t*>(u), M, c.d, c.ln_eps, s, stats);
   else
     launch_layernorm(static_cast<const float*>(x), static_cast<const float*>(g), static_cast<const float*>(b),
                      static_cast<float*>(u), M, c.d, c.ln_eps, s);
@@ -490,7 +492,7 @@ void run_gemm_out(const void* a, int64_t lda, const void* b, int64_t ldb, int64_
 // pass's scratch.  Offsets depend on the call's B*S, so forward_train and backward must be
 // called with the same cfg.
 struct TrainLayout {
-  int64_t u, qkv, ag, f, lse, delta, dyp, dO, dz, du, woT, wiT, dyT, agT, dzT, uT, part, total;
+  int64_t u, qkv, ag, f, lse, stats, delta, dyp, dO, dz, du, woT, wiT, dyT, agT, dzT, uT, part, total;
   int64_t Mp, ln_rows, ln_grid;
 };
 TrainLayout train_layout(const pblock_cfg* c) {
@@ -500,7 +502,7 @@ TrainLayout train_layout(const pblock_cfg* c) {
   const int64_t Mt = m256 + kGemmBM;
   TrainLayout t;
   t.Mp = (M + kGemmBK - 1) / kGemmBK * kGemmBK;  // token count padded to the GEMM's k slab
-  t.ln_rows = std::max<int64_t>(1, (M + 255) / 256);
+  t.ln_rows = std::max<int64_t>(1, (M + 511) / 512);  // about two LayerNorm-backward workgroups per CU
   t.ln_grid = (M + t.ln_rows - 1) / t.ln_rows;
   int64_t o = 0;
   auto take = [&](int64_t bytes) {
@@ -513,6 +515,7 @@ TrainLayout train_layout(const pblock_cfg* c) {
   t.ag = take(Mt * dm.k_out * es);
   t.f = take(M * c->ffn * es);
   t.lse = take(M * c->H * 4);
+  t.stats = take(M * 2 * 4);
   t.delta = take(M * c->H * 4);
   t.dyp = take(m256 * d * es);
   t.dO = take(M * dm.A * es);
@@ -935,7 +938,7 @@ int pblock_forward_train(pblock_t h, const void* x, const pblock_weights* w, con
     Timer tm;
     st = tm.begin(h, s);
     if (st != PBLOCK_OK) return st;
-    run_layernorm(x, w->ln_gamma, w->ln_beta, base + T.u, dm.M, c, s);
+    run_layernorm(x, w->ln_gamma, w->ln_beta, base + T.u, dm.M, c, s, reinterpret_cast<float*>(base + T.stats));
     tm.mark(0);
     InEpi ep;
     ep.pre = base + T.f;
@@ -1051,11 +1054,12 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
       const auto* xp = static_cast<const uint16_t*>(x);
       const auto* gp = static_cast<const uint16_t*>(w->ln_gamma);
       const auto* dup = reinterpret_cast<const float*>(base + T.du);
+      const auto* stp = reinterpret_cast<const float*>(base + T.stats);
       const auto* dyr = c.add_residual ? static_cast<const uint16_t*>(dy) : nullptr;
       auto* dxp = static_cast<uint16_t*>(grads->dx);
       auto* part = reinterpret_cast<float*>(base + T.part);
       const int rows = int(T.ln_rows);
-#define PBLK_LNB(V) hipLaunchKernelGGL((layernorm_bwd_kernel<V>), grid, block, 0, s, xp, gp, dup, dyr, dxp, part, M, int(d), rows, c.ln_eps)
+#define PBLK_LNB(V) hipLaunchKernelGGL((layernorm_bwd_kernel<V>), grid, block, 0, s, xp, gp, dup, dyr, stp, dxp, part, M, int(d), rows)
       if (need <= 1) PBLK_LNB(1);
       else if (need <= 2) PBLK_LNB(2);
       else if (need <= 3) PBLK_LNB(3);
@@ -1063,9 +1067,8 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
       else if (need <= 6) PBLK_LNB(6);
       else PBLK_LNB(8);
 #undef PBLK_LNB
-      hipLaunchKernelGGL(column_sum_kernel, dim3(unsigned((2 * d + 255) / 256)), dim3(256), 0, s, part,
-                         int(T.ln_grid), 2 * d, static_cast<uint16_t*>(grads->dln_gamma),
-                         static_cast<uint16_t*>(grads->dln_beta), d);
+      hipLaunchKernelGGL(column_sum_kernel, dim3(unsigned(2 * d / 64)), dim3(256), 0, s, part, int(T.ln_grid), 2 * d,
+                         static_cast<uint16_t*>(grads->dln_gamma), static_cast<uint16_t*>(grads->dln_beta), d);
     }
     tm.mark(8);
     // token-contiguous operands of the weight-gradient GEMMs (token count padded with zeros)
