@@ -219,8 +219,10 @@ int pblock_forward_variant(pblock_t h, const void* x, const pblock_weights* w, c
  *
  * The training workspace is caller-owned device memory, 256-byte aligned, of at least
  * pblock_train_workspace_bytes(cfg) bytes.  It holds the activations the forward saves
- * (u, q|k|v, [attention | GeLU], the FC1 pre-activation, the per-query log-sum-exp) and the
- * backward's scratch (transposed weights and activations, dz, du, LayerNorm partial sums).
+ * (u, q|k|v, [attention | GeLU], the FC1 pre-activation, the per-query log-sum-exp, the
+ * LayerNorm row statistics) and the backward's scratch (dy in whole 256-row tiles, dO, dz, du,
+ * LayerNorm partial sums).  The gradient GEMMs read the weights and the saved activations in
+ * place (K-major operands), so nothing is transposed.
  * pblock_forward_train and the pblock_backward that consumes it must get the same cfg, x and
  * weights, and the workspace must not be touched in between. */
 typedef struct {
@@ -276,7 +278,7 @@ int pblock_copy_intermediates(pblock_t h, void* u, void* qkv, void* ag, void* st
  * pblock_kernel_times then synchronises on the last recorded event and writes
  * the summed milliseconds per category since the last reset into ms[0 .. n-1]
  * (at most 9), in the order [layernorm, gemm_in, attention, gemm_out,
- * bwd_transpose, bwd_gemm_dgrad, bwd_attention, bwd_gemm_wgrad, bwd_layernorm],
+ * bwd_prep, bwd_gemm_dgrad, bwd_attention, bwd_gemm_wgrad, bwd_layernorm],
  * plus the number of timed calls (the serial form's two LayerNorms count as
  * layernorm, its QKV and FC1 GEMMs as gemm_in, its output-projection and FC2
  * GEMMs as gemm_out).  Enabling or disabling resets the sums.  n must be >= 4. */

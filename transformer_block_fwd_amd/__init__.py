@@ -35,7 +35,7 @@ __all__ = [
 ]
 
 KERNEL_NAMES = ("layernorm", "gemm_in", "attention", "gemm_out")
-BACKWARD_KERNEL_NAMES = ("bwd_transpose", "bwd_gemm_dgrad", "bwd_attention", "bwd_gemm_wgrad", "bwd_layernorm")
+BACKWARD_KERNEL_NAMES = ("bwd_prep", "bwd_gemm_dgrad", "bwd_attention", "bwd_gemm_wgrad", "bwd_layernorm")
 
 _DTYPES = {"bf16": PBLOCK_BF16, "f32": PBLOCK_F32, PBLOCK_BF16: PBLOCK_BF16, PBLOCK_F32: PBLOCK_F32}
 

@@ -1,7 +1,6 @@
 // Elementwise and reduction kernels of the block's backward pass (bf16 storage, fp32 math):
-//   transpose_bf16_kernel   out[c, r] = in[r, c], zero-filled past the source rows, so that the
-//                           weight-gradient GEMMs (a contraction over tokens) see both operands
-//                           token-contiguous with the token count padded to the GEMM's k slab;
+//   zero_kernel             zeroes the token padding (rows M .. Mp-1) the weight-gradient GEMMs
+//                           read as k rows;
 //   layernorm_bwd_kernel    dx = (g - mean(g) - xhat mean(g xhat)) / sigma (+ dy), g = du gamma,
 //                           from the forward's per-row mean and 1/sigma, with per-workgroup
 //                           column partials of du xhat and du;
@@ -34,41 +33,9 @@ __device__ __forceinline__ float gelu_erf_grad(float z) {
   return fmaf(z * 0.3989422804014327f, e, Phi);
 }
 
-// 64 x 64 tiles through LDS; block 256 threads.  in [rows, cols] (row stride ld_in) ->
-// out [cols, out_cols] (row stride ld_out): out[c, r] = in[r, c] for r < rows, 0 for
-// rows <= r < out_cols.  cols and out_cols are multiples of 64, ld_in / ld_out of 8.
-// grid = (out_cols / 64) * (cols / 64).
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t ld_in,
-                                                             int64_t rows, int64_t cols, uint16_t* __restrict__ out,
-                                                             int64_t ld_out, int64_t out_cols) {
-  __shared__ uint16_t tile[64][66];
-  const int64_t tr = out_cols / 64;
-  const int64_t r0 = (blockIdx.x % tr) * 64, c0 = (blockIdx.x / tr) * 64;
-  const int tid = threadIdx.x;
-  // load: 64 rows x 64 columns = 512 pieces of 8; thread t takes pieces t and t + 256
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int piece = tid + 256 * p;
-    const int rr = piece >> 3, cc = (piece & 7) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r0 + rr < rows) v = *reinterpret_cast<const u32x4*>(in + (r0 + rr) * ld_in + c0 + cc);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[rr][cc + 2 * e] = uint16_t(v[e] & 0xFFFFu);
-      tile[rr][cc + 2 * e + 1] = uint16_t(v[e] >> 16);
-    }
-  }
-  __syncthreads();
-  // store: output row c0 + oc holds source column oc for source rows r0 .. r0+63
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int piece = tid + 256 * p;
-    const int oc = piece >> 3, orr = (piece & 7) * 8;
-    u32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = uint32_t(tile[orr + 2 * e][oc]) | (uint32_t(tile[orr + 2 * e + 1][oc]) << 16);
-    *reinterpret_cast<u32x4*>(out + (c0 + oc) * ld_out + r0 + orr) = v;
-  }
+// Zeroes n 16-byte pieces at p (grid-stride).
+__global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
 __device__ __forceinline__ float2 block_sum2_256(float a, float b, float* red) {

@@ -27,6 +27,7 @@
 #include "backward.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
+#include "gemm_kmajor.hpp"
 #include "layernorm.hpp"
 
 using namespace pblk;
@@ -278,8 +279,8 @@ void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, in
   }
 }
 
-// timing categories: layernorm, gemm_in, attention, gemm_out (forward); transpose,
-// gemm_dgrad, attention, gemm_wgrad, layernorm (backward)
+// timing categories: layernorm, gemm_in, attention, gemm_out (forward); prep (dy staged into
+// whole tiles, token padding zeroed), gemm_dgrad, attention, gemm_wgrad, layernorm (backward)
 constexpr int kTimedKernels = 9;
 constexpr int kMaxLaunches = 12;  // launches (or launch groups) of one call that get their own event pair
 constexpr size_t kEventPool = 256;
@@ -492,7 +493,7 @@ void run_gemm_out(const void* a, int64_t lda, const void* b, int64_t ldb, int64_
 // pass's scratch.  Offsets depend on the call's B*S, so forward_train and backward must be
 // called with the same cfg.
 struct TrainLayout {
-  int64_t u, qkv, ag, f, lse, stats, delta, dyp, dO, dz, du, woT, wiT, dyT, agT, dzT, uT, part, total;
+  int64_t u, qkv, ag, f, lse, stats, delta, dyp, dO, dz, du, part, total;
   int64_t Mp, ln_rows, ln_grid;
 };
 TrainLayout train_layout(const pblock_cfg* c) {
@@ -521,23 +522,18 @@ TrainLayout train_layout(const pblock_cfg* c) {
   t.dO = take(M * dm.A * es);
   t.dz = take(m256 * dm.n_in * es);
   t.du = take(M * d * 4);
-  t.woT = take(dm.k_out * d * es);
-  t.wiT = take(d * dm.n_in * es);
-  t.dyT = take((d + kGemmBM - 1) / kGemmBM * kGemmBM * t.Mp * es);
-  t.agT = take(dm.k_out * t.Mp * es);
-  t.dzT = take((dm.n_in + kGemmBM - 1) / kGemmBM * kGemmBM * t.Mp * es);
-  t.uT = take(d * t.Mp * es);
   t.part = take(t.ln_grid * 2 * d * 4);
   t.total = o;
   return t;
 }
 
-// out [cols, out_cols] = in [rows, cols]^T, zero past `rows` (bf16).
-void launch_transpose(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out, int64_t ld_out,
-                      int64_t out_cols, hipStream_t s) {
-  const unsigned grid = unsigned((out_cols / 64) * (cols / 64));
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(grid), dim3(256), 0, s, static_cast<const uint16_t*>(in), ld_in,
-                     rows, cols, static_cast<uint16_t*>(out), ld_out, out_cols);
+// Zeroes rows [r0, r1) of a row-major bf16 matrix with ld columns (ld a multiple of 8): the token
+// padding the weight-gradient GEMMs read as k rows.
+void launch_zero_rows(void* base, int64_t ld, int64_t r0, int64_t r1, hipStream_t s) {
+  if (r1 <= r0) return;
+  const int64_t n16 = (r1 - r0) * ld / 8;  // 16-byte pieces
+  hipLaunchKernelGGL(zero_kernel, dim3(unsigned(std::min<int64_t>((n16 + 255) / 256, 1024))), dim3(256), 0, s,
+                     reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + r0 * ld), n16);
 }
 
 constexpr int kBwdMaxD = 16384;  // LayerNorm backward holds up to 8 vectors of 8 per thread
@@ -993,24 +989,26 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
     st = tm.begin(h, s);
     if (st != PBLOCK_OK) return st;
 
-    // dy into whole 256-row tiles (the GEMM's row operand), W_out^T and W_in^T (K-contiguous
-    // second operands of the two activation-gradient GEMMs)
+    // dy into whole 256-row tiles (the GEMMs' row operand), its token padding zeroed
     hipError_t e = hipMemcpyAsync(base + T.dyp, dy, size_t(M * d * es), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
-    launch_transpose(w->w_out, dm.k_out, d, dm.k_out, base + T.woT, d, d, s);
-    launch_transpose(w->w_in, d, dm.n_in, d, base + T.wiT, dm.n_in, dm.n_in, s);
+    launch_zero_rows(base + T.dyp, d, M, T.Mp, s);
+    launch_zero_rows(base + T.ag, dm.k_out, M, T.Mp, s);
+    launch_zero_rows(base + T.u, d, M, T.Mp, s);
+    launch_zero_rows(base + T.dz, dm.n_in, M, T.Mp, s);
     tm.mark(4);
-    // [dO | dG] = dy W_out; dF = dG * GeLU'(F) straight into dz's FC1 columns
+    // [dO | dG] = dy W_out (W_out read K-major in place); dF = dG * GeLU'(F) straight into dz's
+    // FC1 columns
     {
       GemmArgs g{};
       g.a = reinterpret_cast<const uint16_t*>(base + T.dyp); g.lda = d;
-      g.b = reinterpret_cast<const uint16_t*>(base + T.woT); g.ldb = d;
+      g.b = static_cast<const uint16_t*>(w->w_out); g.ldb = dm.k_out;
       g.M = int(M); g.N = int(dm.k_out); g.K = int(d);
       g.out0 = reinterpret_cast<uint16_t*>(base + T.dO); g.ld0 = A;
       g.out1 = reinterpret_cast<uint16_t*>(base + T.dz); g.ld1 = dm.n_in; g.off1 = 3 * A;
       g.nsplit = int(A);
       g.pre = reinterpret_cast<uint16_t*>(base + T.f); g.ld_pre = c.ffn;
-      launch_gemm_bf16<kEpiGeluBwd>(g, hw.scr, s);
+      launch_gemm_kmajor<kEpiGeluBwd, false>(g, hw.scr.partials, hw.scr.G, s);
     }
     tm.mark(5);
     // attention backward: dQ (and D), then dK, dV, into dz's Q|K|V columns
@@ -1036,15 +1034,15 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
       }
     }
     tm.mark(6);
-    // du = dz W_in (fp32)
+    // du = dz W_in (W_in read K-major in place; fp32 out)
     {
       GemmArgs g{};
       g.a = reinterpret_cast<const uint16_t*>(base + T.dz); g.lda = dm.n_in;
-      g.b = reinterpret_cast<const uint16_t*>(base + T.wiT); g.ldb = dm.n_in;
+      g.b = static_cast<const uint16_t*>(w->w_in); g.ldb = d;
       g.M = int(M); g.N = int(d); g.K = int(dm.n_in);
       g.ld0 = d;
       g.out_f32 = reinterpret_cast<float*>(base + T.du);
-      launch_gemm_bf16<kEpiF32>(g, hw.scr, s);
+      launch_gemm_kmajor<kEpiF32, false>(g, hw.scr.partials, hw.scr.G, s);
     }
     tm.mark(5);
     // LayerNorm backward (+ dy for the residual), dgamma and dbeta
@@ -1071,15 +1069,24 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
                          static_cast<uint16_t*>(grads->dln_gamma), static_cast<uint16_t*>(grads->dln_beta), d);
     }
     tm.mark(8);
-    // token-contiguous operands of the weight-gradient GEMMs (token count padded with zeros)
-    launch_transpose(dy, d, M, d, base + T.dyT, T.Mp, T.Mp, s);
-    launch_transpose(base + T.ag, dm.k_out, M, dm.k_out, base + T.agT, T.Mp, T.Mp, s);
-    launch_transpose(base + T.dz, dm.n_in, M, dm.n_in, base + T.dzT, T.Mp, T.Mp, s);
-    launch_transpose(base + T.u, d, M, d, base + T.uT, T.Mp, T.Mp, s);
-    tm.mark(4);
-    // dW_out = dy^T [A | G], dW_in = dz^T u
-    run_gemm_out(base + T.dyT, T.Mp, base + T.agT, T.Mp, d, dm.k_out, T.Mp, grads->dw_out, nullptr, c.dtype, hw.scr, s);
-    run_gemm_out(base + T.dzT, T.Mp, base + T.uT, T.Mp, dm.n_in, d, T.Mp, grads->dw_in, nullptr, c.dtype, hw.scr, s);
+    // dW_out = dy^T [A | G], dW_in = dz^T u: contractions over the Mp tokens, both operands read
+    // K-major in place (token rows M .. Mp-1 zeroed above)
+    {
+      GemmArgs g{};
+      g.a = reinterpret_cast<const uint16_t*>(base + T.dyp); g.lda = d;
+      g.b = reinterpret_cast<const uint16_t*>(base + T.ag); g.ldb = dm.k_out;
+      g.M = int(d); g.N = int(dm.k_out); g.K = int(T.Mp);
+      g.out0 = static_cast<uint16_t*>(grads->dw_out); g.ld0 = dm.k_out;
+      launch_gemm_kmajor<kEpiResidual, true>(g, hw.scr.partials, hw.scr.G, s);
+    }
+    {
+      GemmArgs g{};
+      g.a = reinterpret_cast<const uint16_t*>(base + T.dz); g.lda = dm.n_in;
+      g.b = reinterpret_cast<const uint16_t*>(base + T.u); g.ldb = d;
+      g.M = int(dm.n_in); g.N = int(d); g.K = int(T.Mp);
+      g.out0 = static_cast<uint16_t*>(grads->dw_in); g.ld0 = d;
+      launch_gemm_kmajor<kEpiResidual, true>(g, hw.scr.partials, hw.scr.G, s);
+    }
     tm.mark(7);
     return launch_status("pblock_backward launch");
   } catch (...) {
