@@ -168,7 +168,7 @@ __device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f3
         for (int e = 0; e < 8; ++e) v[e] = gelu_tanh(v[e]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+        for (int e = 0; e < 8; ++e) v[e] = gelu_erf_bf16out(v[e]);
       }
       dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
     }
