@@ -269,6 +269,33 @@ def test_deterministic_and_reusable_handle():
         tb.pblock_destroy(h)
 
 
+def test_split_k_tails_on_a_reused_handle():
+    """Both GEMMs run entirely as split-K tail tiles at this shape (GEMM-in 8 x 21 = 168 tiles,
+    GEMM-out 8 x 4 = 32, fewer than one wave of 256), through the handle's partial-tile scratch:
+    20 forwards on one handle, every one bit-identical to the first, the first within tolerance
+    of the oracle."""
+    cfg = BlockConfig("tails", B=2, S=1024, d=1024, H=8, hd=128, ffn=2304, W=128, dtype="bf16")
+    inp = make_inputs(cfg, seed=15, affine=True)
+    dev = upload(inp)
+    h = tb.pblock_create(cfg)
+    try:
+        out = torch.empty_like(dev["x"])
+        w = (dev["gamma"], dev["beta"], dev["w_in"], dev["w_out"])
+        tb.pblock_forward(h, dev["x"], w, cfg, out)
+        first = out.clone()
+        for _ in range(19):
+            tb.pblock_forward(h, dev["x"], w, cfg, out)
+            assert bool(torch.equal(out, first))
+        torch.cuda.synchronize()
+    finally:
+        tb.pblock_destroy(h)
+    ref = oracle.block_forward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W,
+                               eps=cfg.ln_eps, add_residual=True)
+    err = rel_err(from_dev(first).reshape(cfg.B, cfg.S, cfg.d), ref)
+    log(f"[parity] split-K tails, reused handle: {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_errors_leave_output_untouched():
     """Rejected calls (through the raw C ABI, past the binding's own checks)
     enqueue nothing: the output keeps its sentinel."""
