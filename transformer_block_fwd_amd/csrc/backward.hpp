@@ -152,9 +152,18 @@ __global__ __launch_bounds__(256) void column_sum_kernel(const float* __restrict
   __shared__ float red[4][64];
   const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int64_t j = int64_t(blockIdx.x) * 64 + c;
-  float s = 0.f;
-  for (int p = g; p < n_part; p += 4) s += partial[int64_t(p) * n + j];
-  red[g][c] = s;
+  // four independent running sums (rows g, g+4, g+8, g+12 mod 16) keep four loads in flight;
+  // the order of every addition is fixed by n_part alone
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int p = g;
+  for (; p + 12 < n_part; p += 16) {
+    s0 += partial[int64_t(p) * n + j];
+    s1 += partial[int64_t(p + 4) * n + j];
+    s2 += partial[int64_t(p + 8) * n + j];
+    s3 += partial[int64_t(p + 12) * n + j];
+  }
+  for (; p < n_part; p += 4) s0 += partial[int64_t(p) * n + j];
+  red[g][c] = (s0 + s1) + (s2 + s3);
   __syncthreads();
   if (g == 0) {
     const float t = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
