@@ -105,7 +105,7 @@ struct GemmSched {
   float* partials;  // [tail * split][kGemmBM][kGemmBN] fp32, row-major partial tile per (tail tile, chunk)
   int tiles_m, tiles_n;
   int KT;           // k slabs per tile
-  int dp_units;     // tiles computed whole (a multiple of the resident workgroup count)
+  int dp_units;     // tiles computed whole (whole waves, or all tiles when a split would be 1)
   int tail;         // tiles computed in k-chunks
   int split;        // k-chunks per tail tile
 };

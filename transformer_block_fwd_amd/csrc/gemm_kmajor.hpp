@@ -250,6 +250,10 @@ void launch_gemm_kmajor(const GemmArgs& g, float* partials, int G, hipStream_t s
   sk.tail = int(T - waves * G);
   sk.dp_units = int(waves * G);
   sk.split = sk.tail > 0 ? int(std::max<int64_t>(1, std::min<int64_t>(G / sk.tail, sk.KT))) : 1;
+  if (sk.split == 1) {  // more than half a wave left over: cutting k would not add workgroups
+    sk.dp_units = int(T);
+    sk.tail = 0;
+  }
   const unsigned grid = unsigned(sk.dp_units + sk.tail * sk.split);
   hipLaunchKernelGGL((gemm_kmajor_kernel<EPI, AK>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
   if (sk.tail > 0)

@@ -224,6 +224,10 @@ Split plan_split(int64_t T, int KT, int G) {
   p.dp_units = int(waves * G);
   p.split = 1;
   if (p.tail > 0) p.split = int(std::max<int64_t>(1, std::min<int64_t>(G / p.tail, KT)));
+  if (p.split == 1) {  // more than half a wave left over: cutting k would not add workgroups
+    p.dp_units = int(T);
+    p.tail = 0;
+  }
   return p;
 }
 
