@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--chunks", type=int, default=0,
                    help="time the forward in this many position chunks (the TP/SP overlap form) with a completion "
                         "event per chunk; per-kernel and roofline figures then come from an unchunked pass")
+    p.add_argument("--chunk-input", action="store_true",
+                   help="with --chunks: pass per-chunk input events too (all steps chunked, the all-gather side "
+                        "of the overlap); without it only the output GEMM is chunked")
     p.add_argument("--gelu-tanh", action="store_true", help="variant: tanh-form GeLU")
     p.add_argument("--bias", action="store_true", help="variant: biases on both projections")
     p.add_argument("--rope", type=float, default=0.0, metavar="BASE",
@@ -280,6 +283,9 @@ def main():
         if args.two_ln:
             oracle_variant.update(gamma2=ln2["gamma2"], beta2=ln2["beta2"])
     done = [torch.cuda.Event(enable_timing=True) for _ in range(args.chunks)]
+    ready = [None] * args.chunks if args.chunk_input else None
+    if args.chunk_input and not args.chunks:
+        raise SystemExit("--chunk-input needs --chunks")
     train_dy = None
     if args.train:
         if args.block != "parallel" or use_variant or args.chunks or cfg.dtype != "bf16":
@@ -301,7 +307,7 @@ def main():
         elif use_variant:
             tb.pblock_forward_variant(h, dev["x"], weights, extra, cfg, variant, out, stream)
         elif chunked:
-            tb.pblock_forward_chunked(h, dev["x"], weights, cfg, out, args.chunks, None, done, stream)
+            tb.pblock_forward_chunked(h, dev["x"], weights, cfg, out, args.chunks, ready, done, stream)
         else:
             tb.pblock_forward(h, dev["x"], weights, cfg, out, stream)
 
@@ -345,7 +351,7 @@ def main():
         kernel_ms, n_fwd = tb.pblock_kernel_times(h)
         tb.pblock_set_timing(h, False)
         unchunked = u0.elapsed_time(u1) / n_un
-        chunking = {"chunks": args.chunks, "chunk_done_ms": [round(v, 5) for v in t_done],
+        chunking = {"chunks": args.chunks, "input_chunked": bool(args.chunk_input), "chunk_done_ms": [round(v, 5) for v in t_done],
                     "unchunked_ms_per_step": round(unchunked, 5),
                     "chunked_over_unchunked": round((ms_total / args.steps) / unchunked, 4)}
         print(f"[bench] chunk completion (ms into the step): {[round(v, 3) for v in t_done]}", file=sys.stderr,

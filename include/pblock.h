@@ -142,14 +142,18 @@ int pblock_forward_serial(pblock_t h, const void* x, const pblock_weights* w, co
  * guided reading, section 3: the GEMMs next to an all-gather or reduce-scatter
  * are split into chunks so that one chunk's communication overlaps the next
  * chunk's computation).  Chunk k covers positions [k*S/n, (k+1)*S/n) (integer
- * division) of every sequence.  For each chunk, in order, on `stream`:
- *   if ready_events and ready_events[k] are non-NULL, wait for that hipEvent_t
- *   (e.g. the arrival of chunk k's rows of x);
+ * division) of every sequence.  With ready_events (an array of n_chunks
+ * hipEvent_t, entries may be NULL), for each chunk, in order, on `stream`:
+ *   wait for ready_events[k] if non-NULL (e.g. the arrival of chunk k's rows of
+ *   x from an all-gather);
  *   LayerNorm, the fused QKV+FC1 GEMM, attention for the chunk's queries (their
  *   keys reach back W-1 positions into earlier chunks) and the output GEMM for
  *   the chunk's rows;
- *   if done_events and done_events[k] are non-NULL, record that hipEvent_t:
+ *   record done_events[k] if done_events and done_events[k] are non-NULL:
  *   chunk k's rows of out are final (the piece a reduce-scatter would send).
+ * With ready_events NULL the input is whole: LayerNorm, the QKV+FC1 GEMM and
+ * attention run once over all rows, then the output GEMM runs chunk by chunk,
+ * recording done_events[k] after each (only the reduce-scatter side is cut).
  * Events are created and owned by the caller.  The result equals
  * pblock_forward's up to floating-point summation order.  1 <= n_chunks <= S
  * (PBLOCK_ERR_ARG otherwise); other rules as pblock_forward.  Per-kernel timing

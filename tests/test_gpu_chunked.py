@@ -40,14 +40,17 @@ def run_chunked(cfg, dev, n_chunks, ready=None, done=None, stream=None):
         tb.pblock_destroy(h)
 
 
+@pytest.mark.parametrize("per_chunk_input", [False, True], ids=["whole_input", "per_chunk_input"])
 @pytest.mark.parametrize("case", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
-def test_chunked_matches_oracle(case):
+def test_chunked_matches_oracle(case, per_chunk_input):
+    """Without input events only the output GEMM is cut into chunks; an input-event array (here
+    all NULL) makes every step run chunk by chunk.  Both match the oracle and the whole forward."""
     name, B, S, d, H, hd, ffn, W, dtype, n = case
     cfg = BlockConfig(name, B=B, S=S, d=d, H=H, hd=hd, ffn=ffn, W=W, dtype=dtype)
-    log(f"[case] chunked x{n} {cfg}")
+    log(f"[case] chunked x{n} per_chunk_input={per_chunk_input} {cfg}")
     inp = make_inputs(cfg, seed=12, affine=True)
     dev = upload(inp)
-    y = run_chunked(cfg, dev, n)
+    y = run_chunked(cfg, dev, n, ready=[None] * n if per_chunk_input else None)
     ref = oracle.block_forward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W,
                                eps=cfg.ln_eps, add_residual=True)
     err = rel_err(y, ref)

@@ -795,24 +795,34 @@ int pblock_forward_chunked(pblock_t h, const void* x, const pblock_weights* w, c
     char* ub = static_cast<char*>(ws.u);
     char* qb = static_cast<char*>(ws.qkv);
     char* ab = static_cast<char*>(ws.ag);
+    if (!ready_events) {
+      // the input is whole: LayerNorm, the input GEMM and attention run once over every row, and
+      // only the output GEMM goes chunk by chunk (the reduce-scatter side of the overlap)
+      run_layernorm(x, w->ln_gamma, w->ln_beta, ws.u, dm.M, c, s);
+      run_gemm_in(ws.u, c.d, w->w_in, c.d, dm.M, dm.n_in, c.d, ws.qkv, 3 * A, ws.ag, dm.k_out, A, 3 * A, c.dtype,
+                  ws.scr, s);
+      launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
+    }
     for (int ck = 0; ck < n_chunks; ++ck) {
       const int p0 = int(int64_t(ck) * c.S / n_chunks), p1 = int(int64_t(ck + 1) * c.S / n_chunks);
       const int64_t rows = p1 - p0;
-      if (ready_events && ready_events[ck]) {
-        hipError_t e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(ready_events[ck]), 0);
-        if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipStreamWaitEvent: ") + hipGetErrorString(e));
+      if (ready_events) {
+        if (ready_events[ck]) {
+          hipError_t e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(ready_events[ck]), 0);
+          if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipStreamWaitEvent: ") + hipGetErrorString(e));
+        }
+        for (int b = 0; b < c.B; ++b) {
+          const int64_t r0 = int64_t(b) * c.S + p0;
+          run_layernorm(xb + r0 * c.d * es, w->ln_gamma, w->ln_beta, ub + r0 * c.d * es, rows, c, s);
+        }
+        for (int b = 0; b < c.B; ++b) {
+          const int64_t r0 = int64_t(b) * c.S + p0;
+          run_gemm_in(ub + r0 * c.d * es, c.d, w->w_in, c.d, rows, dm.n_in, c.d, qb + r0 * 3 * A * es, 3 * A,
+                      ab + r0 * dm.k_out * es, dm.k_out, A, 3 * A, c.dtype, ws.scr, s);
+        }
+        // queries of this chunk; their keys reach back into earlier chunks, already projected
+        launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s, p0, p1);
       }
-      for (int b = 0; b < c.B; ++b) {
-        const int64_t r0 = int64_t(b) * c.S + p0;
-        run_layernorm(xb + r0 * c.d * es, w->ln_gamma, w->ln_beta, ub + r0 * c.d * es, rows, c, s);
-      }
-      for (int b = 0; b < c.B; ++b) {
-        const int64_t r0 = int64_t(b) * c.S + p0;
-        run_gemm_in(ub + r0 * c.d * es, c.d, w->w_in, c.d, rows, dm.n_in, c.d, qb + r0 * 3 * A * es, 3 * A,
-                    ab + r0 * dm.k_out * es, dm.k_out, A, 3 * A, c.dtype, ws.scr, s);
-      }
-      // queries of this chunk; their keys reach back into earlier chunks, already projected
-      launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s, p0, p1);
       for (int b = 0; b < c.B; ++b) {
         const int64_t r0 = int64_t(b) * c.S + p0;
         run_gemm_out(ab + r0 * dm.k_out * es, dm.k_out, w->w_out, dm.k_out, rows, c.d, dm.k_out, ob + r0 * c.d * es,
