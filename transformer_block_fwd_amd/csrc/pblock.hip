@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <array>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -104,21 +105,22 @@ WsLayout ws_layout(const pblock_cfg* c, int G) {
   return w;
 }
 
-// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, -1 no.
-int g_arch_ok[64];
+// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, -1 no (threads may fill it
+// concurrently; they all store the same value).
+std::atomic<int> g_arch_ok[64];
 
 int check_device(int* dev_out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(PBLOCK_ERR_DEVICE, std::string("hipGetDevice: ") + hipGetErrorString(e));
   if (dev < 0 || dev >= 64) return fail(PBLOCK_ERR_DEVICE, "device index out of range");
-  if (g_arch_ok[dev] == 0) {
+  if (g_arch_ok[dev].load(std::memory_order_relaxed) == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(PBLOCK_ERR_DEVICE, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
-    g_arch_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_arch_ok[dev].store((std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1, std::memory_order_relaxed);
   }
-  if (g_arch_ok[dev] != 1) return fail(PBLOCK_ERR_DEVICE, "current device is not gfx950");
+  if (g_arch_ok[dev].load(std::memory_order_relaxed) != 1) return fail(PBLOCK_ERR_DEVICE, "current device is not gfx950");
   if (dev_out) *dev_out = dev;
   return PBLOCK_OK;
 }
