@@ -28,6 +28,23 @@ def from_dev(t) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def scale_q_rows(inp, k: int):
+    """Multiplies the Q rows of W_in by 2^-k in place (exact in bf16 and fp32, so the device and
+    the oracle still see identical values).  Keeps attention scores O(1) for very wide models,
+    where N(0, 0.02^2) weights give scores whose spread grows with sqrt(d)."""
+    from workload import round_to_bf16
+
+    A = inp.cfg.A
+    w = inp.w_in.copy()
+    w[:A] *= np.float32(2.0 ** -k)
+    if inp.bits is not None:
+        vals, bits = round_to_bf16(w)
+        assert np.array_equal(vals, w)
+        inp.bits["w_in"] = bits
+    inp.w_in = w
+    return inp
+
+
 def upload(inp):
     cfg = inp.cfg
     arrs = inp.device_arrays()

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import TOL, from_dev, log, rel_err, run_block, to_dev, upload
+from gpu_helpers import TOL, from_dev, log, rel_err, run_block, scale_q_rows, to_dev, upload
 from workload import CONFIGS, BlockConfig, make_dy, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -24,7 +24,13 @@ SHAPES = [
     ("bwd_w_ge_s", 2, 150, 256, 2, 128, 192, 1000, 1),
     ("bwd_one_token", 1, 1, 128, 1, 64, 64, 4, 1),
     ("bwd_big_ntail", 3, 1100, 1024, 8, 128, 2112, 200, 1),
+    # d = 16384, the largest the backward accepts (Q rows of W_in scaled by 2^-3, see below)
+    ("bwd_max_d", 1, 130, 16384, 2, 64, 128, 40, 1),
 ]
+# For very wide models N(0, 0.02^2) weights give attention scores whose spread grows with
+# sqrt(d) (~6.5 at d = 16384); these shapes scale the Q rows of W_in by an exact power of two
+# so that the scores stay O(1), like the other small shapes.
+Q_SCALE = {"bwd_max_d": 3}
 
 
 def run_train(cfg, dev, dy_dev, handle=None):
@@ -70,6 +76,8 @@ def test_backward_small_full(shape):
     cfg = BlockConfig(name, B=B, S=S, d=d, H=H, hd=hd, ffn=ffn, W=W, dtype="bf16", add_residual=res)
     log(f"[case] backward {cfg}")
     inp = make_inputs(cfg, seed=31, affine=True)
+    if name in Q_SCALE:
+        scale_q_rows(inp, Q_SCALE[name])
     dyd = make_dy(cfg, seed=31)
     dev = upload(inp)
     got = run_train(cfg, dev, to_dev(dyd["dy_dev"], "bf16"))

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import TOL, from_dev, log, rel_err, run_block, to_dev, upload
+from gpu_helpers import TOL, from_dev, log, rel_err, run_block, scale_q_rows, to_dev, upload
 from workload import CONFIGS, BlockConfig, make_inputs, sample_row_blocks
 
 torch = pytest.importorskip("torch")
@@ -117,6 +117,49 @@ def test_large_config_sampled(name):
     ref = np.concatenate(refs)
     err = rel_err(got, ref)
     log(f"[parity] {name}: {len(blocks)} row blocks, rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_largest_model_dim(dtype):
+    """d = 32768, the largest the library accepts: the widest LayerNorm rows (16 or 32 vectors per
+    thread, one row per workgroup), K = 32768 in the input GEMM and N = 32768 in the output GEMM;
+    every output against the oracle, with a ragged token count.  The Q rows of W_in are scaled by
+    2^-3 (exactly): with N(0, 0.02^2) weights the scores at this width would have a spread of ~13,
+    where the bf16 storage of q and k alone moves the softmax by more than the tolerance."""
+    cfg = BlockConfig("max_d_" + dtype, B=1, S=130, d=32768, H=2, hd=64, ffn=128, W=40, dtype=dtype)
+    log(f"[case] {cfg}")
+    inp = scale_q_rows(make_inputs(cfg, seed=21, affine=True), 3)
+    y = run_block(cfg, upload(inp))
+    err = rel_err(y, oracle_y(inp))
+    log(f"[parity] {cfg.name}: rel err {err:.3e} (tol {TOL[dtype]})")
+    assert err <= TOL[dtype]
+
+
+def test_largest_token_count_sampled():
+    """B*S = 2^24 tokens, the largest the library accepts (16 sequences of 2^20): element offsets
+    into QKV pass 2^31, so every index on the path must be 64-bit.  Row blocks at the start and
+    end of the first and last sequences against the oracle, computed one by one."""
+    cfg = BlockConfig("max_tokens", B=16, S=1 << 20, d=64, H=1, hd=64, ffn=64, W=64, dtype="bf16")
+    log(f"[case] {cfg}")
+    inp = make_inputs(cfg, seed=22, affine=True)
+    dev = upload(inp)
+    h = tb.pblock_create(cfg)
+    try:
+        out = torch.empty_like(dev["x"])
+        tb.pblock_forward(h, dev["x"], (dev["gamma"], dev["beta"], dev["w_in"], dev["w_out"]), cfg, out)
+        torch.cuda.synchronize()
+        S = cfg.S
+        blocks = [(0, 0, 32), (0, S - 32, S), (15, 0, 32), (15, S // 2, S // 2 + 32), (15, S - 32, S)]
+        got = np.concatenate([from_dev(out[b, i0:i1]) for b, i0, i1 in blocks])
+    finally:
+        tb.pblock_destroy(h)
+        del dev
+        torch.cuda.empty_cache()
+    refs = oracle.block_forward_rows(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W, blocks,
+                                     eps=cfg.ln_eps, add_residual=True)
+    err = rel_err(got, np.concatenate(refs))
+    log(f"[parity] max_tokens: {len(blocks)} row blocks, rel err {err:.3e}")
     assert err <= TOL["bf16"]
 
 

@@ -70,8 +70,9 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 // workgroup normalizes rows_per_wg consecutive rows; `stats` (optional, [M][2]) receives each
 // row's mean and 1/sigma.  For rows of up to 2048 vectors
 // (VPT <= 8) gamma and beta stay in registers across the rows and the next row's loads
-// are in flight while the current one is reduced and written; wider rows take one row
-// per workgroup (the host passes rows_per_wg = 1) and read gamma and beta per row.
+// are in flight while the current one is reduced and written; wider rows are loaded one
+// at a time (the host gives them one row per workgroup unless the grid would exceed the
+// launch limit) and read gamma and beta per row.
 template <typename T, int VPT>
 __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
                                                                const T* __restrict__ beta, T* __restrict__ u,
@@ -159,6 +160,8 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restri
     if constexpr (kHold) {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
+    } else if (row + 1 < row_end) {
+      load_row(row + 1, cur);
     }
   }
 }

@@ -183,6 +183,8 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(int iters, float* sin
 
 // ------------------------------------------------------------------------ launches
 
+constexpr int64_t kMaxGridWgs = (int64_t(1) << 24) - 1;  // workgroups of 256 in one launch
+
 template <typename T>
 void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d, float eps, hipStream_t s,
                       float* stats = nullptr) {
@@ -193,7 +195,9 @@ void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d
   // wider than 8 vectors per thread go one per workgroup.
   const int64_t row_bytes = int64_t(d) * int64_t(sizeof(T));
   const int want = row_bytes >= 16384 ? kLnMaxRows : (row_bytes >= 4096 ? 2 : 1);
-  const int rows = need > 8 ? 1 : int(std::max<int64_t>(1, std::min<int64_t>(want, M / 512)));
+  int rows = need > 8 ? 1 : int(std::max<int64_t>(1, std::min<int64_t>(want, M / 512)));
+  // a launch holds fewer than 2^32 work-items: at most 2^24 - 1 workgroups of 256
+  rows = int(std::max<int64_t>(rows, (M + kMaxGridWgs - 1) / kMaxGridWgs));
   const dim3 grid{static_cast<unsigned>((M + rows - 1) / rows)}, block{kLnThreads};
 #define PBLK_LN(V) hipLaunchKernelGGL((layernorm_kernel<T, V>), grid, block, 0, s, x, g, b, u, M, d, rows, eps, stats)
   if (need <= 1) PBLK_LN(1);
