@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(int iters, float* sin
       h ^= h >> 15;
       h *= 0x2c1b3c6du;
       h ^= h >> 12;
-      ua[e] = h & 0x3F7F3F7Fu;  // two bf16 values in (-2, 2)
+      ua[e] = h & 0x3F7F3F7Fu;  // two bf16 values in [0, 1) (sign and top exponent bits cleared)
       ub[e] = (h >> 1) & 0x3F7F3F7Fu;
     }
     a[i] = __builtin_bit_cast(bf16x8, ua);
