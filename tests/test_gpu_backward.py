@@ -24,6 +24,10 @@ SHAPES = [
     ("bwd_w_ge_s", 2, 150, 256, 2, 128, 192, 1000, 1),
     ("bwd_one_token", 1, 1, 128, 1, 64, 64, 4, 1),
     ("bwd_big_ntail", 3, 1100, 1024, 8, 128, 2112, 200, 1),
+    # B*S a multiple of 256: dy is read in place as the GEMMs' row operand (no staging copy);
+    # d = 192 also has the K-major dy reads clamp at the last 8 columns
+    ("bwd_whole_tiles", 2, 256, 256, 2, 128, 320, 64, 1),
+    ("bwd_whole_tiles_d192", 1, 768, 192, 3, 64, 128, 100, 0),
     # d = 16384, the largest the backward accepts (Q rows of W_in scaled by 2^-3, see below)
     ("bwd_max_d", 1, 130, 16384, 2, 64, 128, 40, 1),
 ]
@@ -176,7 +180,9 @@ def test_backward_timing_categories():
             run_train(cfg, dev, dy, handle=h)
         ms, n = tb.pblock_kernel_times(h, backward=True)
         assert n == 4  # two forward_train and two backward calls
-        assert all(v > 0 for v in ms.values()), ms
+        # B*S = 256 fills whole GEMM tiles: dy is read in place and the staging step is empty
+        assert all(v > 0 for k, v in ms.items() if k != "bwd_prep"), ms
+        assert ms["bwd_prep"] >= 0, ms
         torch.cuda.synchronize()
     finally:
         tb.pblock_destroy(h)

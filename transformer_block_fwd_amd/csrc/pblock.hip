@@ -1009,10 +1009,15 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
     st = tm.begin(h, s);
     if (st != PBLOCK_OK) return st;
 
-    // dy into whole 256-row tiles (the GEMMs' row operand), its token padding zeroed
-    hipError_t e = hipMemcpyAsync(base + T.dyp, dy, size_t(M * d * es), hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
-    launch_zero_rows(base + T.dyp, d, M, T.Mp, s);
+    // dy as the GEMMs' row operand: read in place when B*S fills whole 256-row tiles (no row
+    // past M is read then), else copied into whole tiles with its token padding zeroed
+    const void* dy_rows = dy;
+    if (M % kGemmBM != 0) {
+      hipError_t e = hipMemcpyAsync(base + T.dyp, dy, size_t(M * d * es), hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return fail(PBLOCK_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
+      launch_zero_rows(base + T.dyp, d, M, T.Mp, s);
+      dy_rows = base + T.dyp;
+    }
     launch_zero_rows(base + T.ag, dm.k_out, M, T.Mp, s);
     launch_zero_rows(base + T.u, d, M, T.Mp, s);
     launch_zero_rows(base + T.dz, dm.n_in, M, T.Mp, s);
@@ -1021,7 +1026,7 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
     // FC1 columns
     {
       GemmArgs g{};
-      g.a = reinterpret_cast<const uint16_t*>(base + T.dyp); g.lda = d;
+      g.a = static_cast<const uint16_t*>(dy_rows); g.lda = d;
       g.b = static_cast<const uint16_t*>(w->w_out); g.ldb = dm.k_out;
       g.M = int(M); g.N = int(dm.k_out); g.K = int(d);
       g.out0 = reinterpret_cast<uint16_t*>(base + T.dO); g.ld0 = A;
@@ -1093,7 +1098,7 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
     // K-major in place (token rows M .. Mp-1 zeroed above)
     {
       GemmArgs g{};
-      g.a = reinterpret_cast<const uint16_t*>(base + T.dyp); g.lda = d;
+      g.a = static_cast<const uint16_t*>(dy_rows); g.lda = d;
       g.b = reinterpret_cast<const uint16_t*>(base + T.ag); g.ldb = dm.k_out;
       g.M = int(d); g.N = int(dm.k_out); g.K = int(T.Mp);
       g.out0 = static_cast<uint16_t*>(grads->dw_out); g.ld0 = dm.k_out;
