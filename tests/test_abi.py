@@ -42,6 +42,8 @@ def test_header_symbols_exported():
 def test_binding_names_match_abi():
     for n in header_functions():
         assert hasattr(tb, n), n
+    # and lists them among its public names
+    assert set(header_functions()) <= set(tb.__all__), set(header_functions()) - set(tb.__all__)
 
 
 def test_validate_accepts_all_workloads():

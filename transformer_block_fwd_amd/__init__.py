@@ -32,6 +32,7 @@ __all__ = [
     "pblock_kernel_times", "pblock_swa_attention", "pblock_strerror", "pblock_last_error", "KERNEL_NAMES",
     "PblockVariant", "PblockVariantWeights", "make_variant", "pblock_forward_variant",
     "PblockGrads", "pblock_train_workspace_bytes", "pblock_forward_train", "pblock_backward",
+    "pblock_forward_serial", "pblock_forward_chunked", "pblock_mfma_loop", "as_cfg", "BACKWARD_KERNEL_NAMES",
 ]
 
 KERNEL_NAMES = ("layernorm", "gemm_in", "attention", "gemm_out")
