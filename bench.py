@@ -220,8 +220,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); the block is "
-              "measured on one GPU's share at its real shape. Run with --gpus 1.", file=sys.stderr, flush=True)
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): the block runs on one GPU's "
+              "share at its real shape, and the library has no collectives. Run with --gpus 1.", file=sys.stderr,
+              flush=True)
         sys.exit(2)
 
     import numpy as np  # noqa: F401
