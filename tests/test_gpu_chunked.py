@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from gpu_helpers import TOL, from_dev, log, rel_err, run_block, upload
-from workload import BlockConfig, make_inputs
+from workload import CONFIGS, BlockConfig, make_inputs, sample_row_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +60,39 @@ def test_chunked_matches_oracle(case, per_chunk_input):
     err2 = rel_err(y, y_whole)
     log(f"[parity] {name}: chunked vs whole {err2:.3e}")
     assert err2 <= TOL[dtype]
+
+
+_SHARD_REF: dict = {}  # oracle rows of the 175B shard workload, by (b, i0, i1)
+
+
+@pytest.mark.parametrize("per_chunk_input", [False, True], ids=["whole_input", "per_chunk_input"])
+@pytest.mark.parametrize("n_chunks", [4, 8])
+def test_chunked_shard175b_sampled(n_chunks, per_chunk_input):
+    """The 175B shard workload in the chunked launch configurations the benchmark times (4 and 8
+    chunks, with and without per-chunk input): sampled row blocks against the oracle, plus a row
+    block across every chunk boundary, where a chunk's windows reach back into the one before."""
+    import torch
+
+    cfg = CONFIGS["shard175b"]
+    log(f"[case] shard175b chunked x{n_chunks} per_chunk_input={per_chunk_input}")
+    inp = make_inputs(cfg, seed=0)
+    dev = upload(inp)
+    y = run_chunked(cfg, dev, n_chunks, ready=[None] * n_chunks if per_chunk_input else None)
+    del dev
+    torch.cuda.empty_cache()
+    assert np.isfinite(y).all()
+    bounds = [ck * cfg.S // n_chunks for ck in range(1, n_chunks)]
+    blocks = sorted(set(sample_row_blocks(cfg)) | {(0, p - 16, p + 16) for p in bounds})
+    todo = [blk for blk in blocks if blk not in _SHARD_REF]
+    if todo:
+        refs = oracle.block_forward_rows(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W,
+                                         todo, eps=cfg.ln_eps, add_residual=bool(cfg.add_residual))
+        _SHARD_REF.update(zip(todo, refs))
+    got = np.concatenate([y[b, i0:i1] for b, i0, i1 in blocks])
+    ref = np.concatenate([_SHARD_REF[blk] for blk in blocks])
+    err = rel_err(got, ref)
+    log(f"[parity] shard175b chunked x{n_chunks}: {len(blocks)} row blocks, rel err {err:.3e}")
+    assert err <= TOL["bf16"]
 
 
 def test_done_events_in_order():
