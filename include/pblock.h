@@ -65,8 +65,8 @@ typedef enum { PBLOCK_F32 = 0, PBLOCK_BF16 = 1 } pblock_dtype;
 
 /* Block shape.  Supported ranges (else PBLOCK_ERR_SHAPE):
  *   B >= 1, S >= 1, B*S <= 2^24;  W >= 1 (W >= S means full causal);
- *   hd in {64, 128};  H >= 1;  d, H*hd, ffn positive multiples of 64;
- *   d <= 32768.
+ *   hd in {64, 128};  1 <= H <= 4096;  d, H*hd, ffn positive multiples of 64;
+ *   d <= 32768, H*hd <= 2^20, ffn <= 2^20.
  * add_residual: 1 -> y = x + branches; 0 -> y = branches only (the partial
  * sum one tensor-parallel shard contributes to the reduce-scatter).
  * ln_eps > 0. */
@@ -111,7 +111,9 @@ double pblock_flops(const pblock_cfg* cfg);
 int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle);
 
 /* Enqueues the block forward on `stream` (a hipStream_t; NULL = the null
- * stream) and returns without synchronising.  x, the weights and out are
+ * stream) and returns without synchronising.  It enqueues kernels only (no
+ * allocation, no host synchronisation, no memset), so a caller may capture
+ * it in a HIP graph and replay it.  x, the weights and out are
  * device pointers owned by the caller; they must stay valid until the stream
  * passes this work.  cfg must equal the create cfg except that B and S may
  * differ as long as B*S does not exceed the create cfg's B*S.  A handle's
@@ -224,8 +226,9 @@ int pblock_forward_variant(pblock_t h, const void* x, const pblock_weights* w, c
  * The training workspace is caller-owned device memory, 256-byte aligned, of at least
  * pblock_train_workspace_bytes(cfg) bytes.  It holds the activations the forward saves
  * (u, q|k|v, [attention | GeLU], the FC1 pre-activation, the per-query log-sum-exp, the
- * LayerNorm row statistics) and the backward's scratch (dy in whole 256-row tiles, dO, dz, du,
- * LayerNorm partial sums).  The gradient GEMMs read the weights and the saved activations in
+ * LayerNorm row statistics) and the backward's scratch (dy copied into whole 256-row tiles when
+ * B*S is not a multiple of 256 -- otherwise dy is read in place --, dO, dz, du, LayerNorm
+ * partial sums).  The gradient GEMMs read the weights and the saved activations in
  * place (K-major operands), so nothing is transposed.
  * pblock_forward_train and the pblock_backward that consumes it must get the same cfg, x and
  * weights, and the workspace must not be touched in between. */
