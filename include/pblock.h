@@ -288,7 +288,12 @@ int pblock_copy_intermediates(pblock_t h, void* u, void* qkv, void* ag, void* st
  * bwd_prep, bwd_gemm_dgrad, bwd_attention, bwd_gemm_wgrad, bwd_layernorm],
  * plus the number of timed calls (the serial form's two LayerNorms count as
  * layernorm, its QKV and FC1 GEMMs as gemm_in, its output-projection and FC2
- * GEMMs as gemm_out).  Enabling or disabling resets the sums.  n must be >= 4. */
+ * GEMMs as gemm_out).  Enabling or disabling resets the sums.  n must be >= 4.
+ * The events come from a pool of 256 calls per handle: when it is used up, the
+ * next timed call first synchronises on the recorded events and folds them
+ * into the sums, so with timing on, every 256th call waits for the earlier
+ * ones to finish.  Timing off (the default) records nothing and never waits.
+ * Not for calls under graph capture. */
 int pblock_set_timing(pblock_t h, int enable);
 int pblock_kernel_times(pblock_t h, float* ms, int n, int* n_forwards);
 
