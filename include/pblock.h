@@ -251,7 +251,8 @@ int pblock_forward_train(pblock_t h, const void* x, const pblock_weights* w, con
 /* Gradients for the output gradient dy [B, S, d] of the forward that pblock_forward_train saved
  * in ws: every pointer of *grads is written (fp32 accumulation, one bf16 rounding of each
  * result; dx, dgamma and dbeta see du in fp32).  The gradients must not overlap each other,
- * x, dy, a weight or ws (PBLOCK_ERR_ALIAS); all 16-byte aligned.  Enqueued on `stream`. */
+ * x, dy, a weight or ws, and dy must not overlap ws (PBLOCK_ERR_ALIAS); all 16-byte aligned.
+ * Enqueued on `stream`. */
 int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, const void* dy,
                     const pblock_grads* grads, void* ws, int64_t ws_bytes, void* stream);
 

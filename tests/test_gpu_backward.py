@@ -155,6 +155,10 @@ def test_backward_rejections():
         assert call(ws.data_ptr(), need, gg=g_alias) == _abi.PBLOCK_ERR_ALIAS
         g_ws = _abi.PblockGrads(ws.data_ptr() + 1024, g.dln_gamma, g.dln_beta, g.dw_in, g.dw_out)
         assert call(ws.data_ptr(), need, gg=g_ws) == _abi.PBLOCK_ERR_ALIAS
+        # dy inside the workspace (dy may be read in place while the scratch is written)
+        assert f(ctypes.c_void_p(h), ctypes.c_void_p(dev["x"].data_ptr()), ctypes.byref(w), ctypes.byref(c),
+                 ctypes.c_void_p(ws.data_ptr() + 4096), ctypes.byref(g), ctypes.c_void_p(ws.data_ptr()), need,
+                 None) == _abi.PBLOCK_ERR_ALIAS
         c32 = tb.as_cfg(cfg.replace(dtype="f32"))
         assert _abi.lib().pblock_train_workspace_bytes(ctypes.byref(c32)) == _abi.PBLOCK_ERR_DTYPE
         torch.cuda.synchronize()

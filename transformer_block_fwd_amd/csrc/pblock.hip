@@ -993,6 +993,8 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
         {x, M * d * es}, {dy, M * d * es}, {w->w_in, dm.n_in * d * es}, {w->w_out, d * dm.k_out * es},
         {w->ln_gamma, d * es}, {w->ln_beta, d * es}, {ws, T.total}};
     if (!aligned16(dy)) return fail(PBLOCK_ERR_ALIGN, "dy must be 16-byte aligned");
+    // dy may be read in place while the backward writes its scratch into ws
+    if (overlap(dy, M * d * es, ws, T.total)) return fail(PBLOCK_ERR_ALIAS, "dy overlaps the training workspace");
     for (int i = 0; i < 5; ++i) {
       if (!aligned16(outs[i].p)) return fail(PBLOCK_ERR_ALIGN, "gradient pointers must be 16-byte aligned");
       for (const auto& in : ins)
