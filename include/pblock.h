@@ -123,10 +123,10 @@ int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pbl
                    void* out, void* stream);
 
 /* The standard (serial) layer the parallel block replaces, built from the same
- * kernels for comparison (MegaScale guided reading, section 2: in a standard
- * layer the attention sub-layer runs first and the feed-forward sub-layer
- * consumes its output; section 8, Table 3 prices the parallel form at +4.6 MFU
- * points).  Pre-LayerNorm form:
+ * kernels for comparison (MegaScale guided reading, section 2: the usual layer
+ * is sequential, its feed-forward part taking the attention part's result as
+ * input; section 8, Table 3 prices the parallel form at +4.6 MFU points).
+ * Pre-LayerNorm form:
  *   h = x + Attn(LN1(x)),   y = h + W2 GeLU(W1 LN2(h))
  * LN1 = (w->ln_gamma, w->ln_beta), LN2 = (ln2_gamma, ln2_beta), both [d].  The
  * attention sub-layer uses W_in rows [0, 3*H*hd) and W_out columns [0, H*hd),
@@ -217,8 +217,8 @@ int pblock_forward_variant(pblock_t h, const void* x, const pblock_weights* w, c
 
 /* ---- Training: forward with saved activations, and the backward pass ----
  * The pages' setting is training; the backward pass mirrors the forward (MegaScale guided
- * reading, section 3: what the parallel block and the overlap do in the forward pass "is
- * done in the backward pass" too).  Gradients of L = sum(dy * y) by the chain rule through
+ * reading, section 3: the overlap of the forward pass carries over to the backward pass as
+ * well).  Gradients of L = sum(dy * y) by the chain rule through
  * LayerNorm, the input projection, the sliding-window softmax attention (FlashAttention-2
  * style: softmax weights recomputed from the saved log-sum-exp), GeLU and the output
  * projection.  bf16 only (PBLOCK_ERR_DTYPE otherwise), d <= 16384 (PBLOCK_ERR_SHAPE).
@@ -303,9 +303,32 @@ int pblock_kernel_times(pblock_t h, float* ms, int n, int* n_forwards);
  *        V at [2*H*hd, 3*H*hd); ld_qkv >= 3*H*hd, a multiple of 8.
  *   o    [B*S, ld_o]: head h written to columns [h*hd, (h+1)*hd); ld_o >= H*hd,
  *        a multiple of 8.
+ * Both strides at most 2^24 elements (PBLOCK_ERR_SHAPE otherwise: the kernels address
+ * a tile of 64 rows with 32-bit offsets).  W >= S is full causal attention.
  * dtype as above; hd in {64, 128}.  Enqueued on `stream`, no sync. */
 int pblock_swa_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, int32_t B, int32_t S,
                          int32_t H, int32_t hd, int32_t W, int32_t dtype, void* stream);
+
+/* The GeLU forms the kernels' epilogues evaluate, on their own (an inspection entry: the
+ * block's GeLU is exact erf GeLU per the readings above, and these are the device
+ * approximations of it that the tests hold to their published error bounds):
+ *   PBLOCK_ACT_GELU_ERF_F32   fp32 path: z Phi(z) with erfc from Numerical Recipes' erfcc
+ *                             (2nd ed., section 6.2; fractional error of erfc < 1.2e-7);
+ *   PBLOCK_ACT_GELU_ERF_BF16  bf16 path: z Phi(z) with erfc from Abramowitz and Stegun 7.1.26
+ *                             (absolute error of erf < 1.5e-7);
+ *   PBLOCK_ACT_GELU_TANH      the tanh form of the variant switch (Hendrycks and Gimpel);
+ *   PBLOCK_ACT_GELU_ERF_GRAD  the backward pass's Phi(z) + z phi(z), A&S 7.1.26 for Phi.
+ * z and out: n fp32 values each, device memory owned by the caller; out may equal z (in
+ * place) but must not overlap it otherwise (PBLOCK_ERR_ALIAS).  0 <= n <= 2^40
+ * (PBLOCK_ERR_SHAPE); an unknown form gives PBLOCK_ERR_ARG.  Enqueued on `stream`, no
+ * sync. */
+enum {
+  PBLOCK_ACT_GELU_ERF_F32 = 0,
+  PBLOCK_ACT_GELU_ERF_BF16 = 1,
+  PBLOCK_ACT_GELU_TANH = 2,
+  PBLOCK_ACT_GELU_ERF_GRAD = 3
+};
+int pblock_activation(const float* z, float* out, int64_t n, int32_t form, void* stream);
 
 /* Measurement aid, not part of the block: a register-only loop of
  * v_mfma_f32_32x32x16_bf16 (the GEMMs' instruction) on `workgroups` workgroups

@@ -194,8 +194,8 @@ def block_forward_rows(x, gamma, beta, w_in, w_out, H: int, hd: int, W: int, row
 def serial_block_forward(x, gamma, beta, gamma2, beta2, w_in, w_out, H: int, hd: int, W: int,
                          eps: float = 1e-5):
     """The standard (serial) layer the parallel block replaces, in pre-LayerNorm form
-    (MegaScale guided reading, section 2: in a standard layer the attention sub-layer
-    runs first and the feed-forward sub-layer consumes its output):
+    (MegaScale guided reading, section 2: the usual layer is sequential, its
+    feed-forward part taking the attention part's result as input):
 
         h = x + Attn_SWA(LN1 x) W_o^T
         y = h + GeLU(LN2(h) W_1^T) W_2^T
@@ -243,7 +243,7 @@ def serial_block_forward_rows(x, gamma, beta, gamma2, beta2, w_in, w_out, H: int
 
 
 # ----------------------------------------------------------------------------- backward pass
-# The pages' context is training ("the same is done in the backward pass", section 3): the
+# The pages' context is training (section 3 carries the forward's scheme over to the backward): the
 # gradients of the block's loss with respect to its input and parameters, given the gradient
 # dy of its output, by the chain rule through each step of block_forward.
 

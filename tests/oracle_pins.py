@@ -677,7 +677,40 @@ def pin_block_backward_w1(ob):
     assert np.abs(dw_in[2 * A:3 * A]).min() > 0.0 and np.abs(dw_in[3 * A:]).max() > 1e-3
 
 
+def pin_relative_error(ob):
+    """The parity metric max|y_test - y_ref| / max|y_ref|, on hand-worked values: the
+    denominator is the reference's largest magnitude (not the tested array's), the numerator
+    the largest elementwise difference (not a mean, not a per-element ratio); swapping the
+    arguments changes the value; an all-zero reference gives the absolute error."""
+    ref = np.array([[1.0, 2.0], [3.0, -4.0]])
+    test = np.array([[1.0, 2.0], [3.0, -4.4]])
+    # max |diff| = 0.4 at the reference's largest element, max |ref| = 4
+    assert abs(ob.relative_error(test, ref) - 0.1) < 1e-15
+    # a difference away from the largest element: 0.25 / 4
+    test2 = np.array([[1.25, 2.0], [3.0, -4.0]])
+    assert abs(ob.relative_error(test2, ref) - 0.0625) < 1e-15
+    # swapped arguments: max |diff| = 4, divided by max |ref| = 2 or by max |test| = 6
+    a, b = np.array([1.0, 6.0]), np.array([1.0, 2.0])
+    assert abs(ob.relative_error(a, b) - 2.0) < 1e-15
+    assert abs(ob.relative_error(b, a) - 4.0 / 6.0) < 1e-15
+    # all-zero reference: the absolute error
+    assert ob.relative_error(np.array([0.5, -0.75]), np.zeros(2)) == 0.75
+    assert ob.relative_error(np.zeros(3), np.zeros(3)) == 0.0
+    # equal arrays, any shape: 0; scaling both by c > 0 leaves the value unchanged
+    rng = _rng(40)
+    x = rng.standard_normal((3, 5, 7))
+    y = x + 1e-3 * rng.standard_normal(x.shape)
+    assert ob.relative_error(x, x) == 0.0
+    r = ob.relative_error(y, x)
+    assert abs(ob.relative_error(8.0 * y, 8.0 * x) - r) < 1e-15
+    # brute force over the elements in plain Python
+    num = max(abs(float(p) - float(q)) for p, q in zip(y.ravel(), x.ravel()))
+    den = max(abs(float(q)) for q in x.ravel())
+    assert abs(r - num / den) < 1e-15
+
+
 ALL_PINS = [
+    pin_relative_error,
     pin_attention_brute_force,
     pin_attention_vs_torch_band,
     pin_attention_full_causal,

@@ -96,7 +96,7 @@ def test_backward_small_full(shape):
 # At the 175B shard shape the attention scores have a standard deviation of ~4.9 (max ~29), so
 # the bf16 storage of u and of q, k, v (2^-9 relative each) already moves the exact attention
 # output by 1.64e-2 of its maximum: the fp64 oracle fed the bf16-rounded u, q, k, v lands there
-# (a CPU-only computation).  Every gradient inherits that floor through the stored attention
+# (tests/test_precision_floor.py computes it on the CPU).  Every gradient inherits that floor through the stored attention
 # output (dW_out), D = dO.O and dS, so the bar for this shape is 2e-2; the small shapes, whose
 # scores are O(0.1), keep the 1e-2 of the forward.
 TOL_BWD_SHARD = 2e-2
@@ -117,6 +117,23 @@ def test_backward_shard175b_full():
     ref = oracle.block_backward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, dyd["dy"], cfg.H, cfg.hd, cfg.W,
                                 eps=cfg.ln_eps, add_residual=bool(cfg.add_residual))
     check_grads("shard175b", got, ref, TOL_BWD_SHARD)
+
+
+def test_window_at_int32_max_is_full_causal():
+    """W = 2^31 - 1, the largest window the cfg can hold, is full causal attention: the forward
+    and every gradient are bit-identical to W = S (the window sums never overflow)."""
+    cfg = BlockConfig("w_max", B=2, S=300, d=256, H=2, hd=128, ffn=256, W=300, dtype="bf16")
+    inp = make_inputs(cfg, seed=33, affine=True)
+    dyd = make_dy(cfg, seed=33)
+    dev = upload(inp)
+    dy = to_dev(dyd["dy_dev"], "bf16")
+    got_s = run_train(cfg, dev, dy)
+    got_max = run_train(cfg.replace(W=2 ** 31 - 1), dev, dy)
+    for k in ("y",) + GRAD_KEYS:
+        assert np.array_equal(got_s[k], got_max[k]), k
+    ref = oracle.block_backward(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, dyd["dy"], cfg.H, cfg.hd, cfg.S,
+                                eps=cfg.ln_eps, add_residual=True)
+    check_grads("w_max", got_max, ref, TOL["bf16"])
 
 
 def test_backward_rejections():

@@ -1,17 +1,17 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Bar: max|y_gpu - y_ref| / max|y_ref| <= 1e-2 for bf16 and <= 1e-4 for fp32,
-elementwise over every output (small shapes) or over sampled row blocks that
-the oracle computes one by one (full-size workloads, in the same launch
-configuration the benchmark times).  Invariants that hold at any size are
+elementwise over every output, for the small shapes and for the full-size
+workloads in the launch configuration the benchmark times (only the 2^24-token
+limit case compares row blocks the oracle computes one by one).  Invariants that hold at any size are
 checked bit-for-bit where the arithmetic makes them exact.
 """
 import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import TOL, from_dev, log, rel_err, run_block, scale_q_rows, to_dev, upload
-from workload import CONFIGS, BlockConfig, make_inputs, sample_row_blocks
+from gpu_helpers import TOL, from_dev, log, oracle_y_cached, rel_err, run_block, scale_q_rows, to_dev, upload
+from workload import CONFIGS, BlockConfig, make_inputs
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -84,7 +84,7 @@ def test_tiny_config_fp32():
     inp = make_inputs(cfg, seed=0)
     y = run_block(cfg, upload(inp))
     err = rel_err(y, oracle_y(inp))
-    log(f"[parity] tiny: {err:.3e}")
+    log(f"[parity] tiny: all {y.size} outputs, rel err {err:.3e} (tol {TOL['f32']})")
     assert err <= TOL["f32"]
 
 
@@ -94,14 +94,14 @@ def test_small_config_full():
     inp = make_inputs(cfg, seed=0)
     y = run_block(cfg, upload(inp))
     err = rel_err(y, oracle_y(inp))
-    log(f"[parity] small: {err:.3e}")
+    log(f"[parity] small: all {y.size} outputs, rel err {err:.3e} (tol {TOL['bf16']})")
     assert err <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("name", ["shard175b", "long", "fullcausal"])
-def test_large_config_sampled(name):
-    """Full-size workloads: sampled row blocks (sequence start, first full
-    window, a random block, sequence end; first and last batch)."""
+def test_large_config_full(name):
+    """Full-size workloads in the launch configuration the benchmark times: every output
+    element against the oracle's full forward."""
     cfg = CONFIGS[name]
     log(f"[case] {cfg}")
     inp = make_inputs(cfg, seed=0)
@@ -110,13 +110,8 @@ def test_large_config_sampled(name):
     del dev
     torch.cuda.empty_cache()
     assert np.isfinite(y).all()
-    blocks = sample_row_blocks(cfg)
-    refs = oracle.block_forward_rows(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W, blocks,
-                                     eps=cfg.ln_eps, add_residual=bool(cfg.add_residual))
-    got = np.concatenate([y[b, i0:i1] for b, i0, i1 in blocks])
-    ref = np.concatenate(refs)
-    err = rel_err(got, ref)
-    log(f"[parity] {name}: {len(blocks)} row blocks, rel err {err:.3e}")
+    err = rel_err(y, oracle_y_cached(inp, 0))
+    log(f"[parity] {name}: all {y.size} outputs, rel err {err:.3e} (tol {TOL['bf16']})")
     assert err <= TOL["bf16"]
 
 

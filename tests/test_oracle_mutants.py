@@ -69,6 +69,10 @@ MUTANTS = {
     "residual_grad_dropped": [("        dx = dx + dy\n", "        dx = dx\n")],
     "dw_out_before_gelu": [("dw_out = dy.reshape(-1, d).T @ ag.reshape(-1, ag.shape[-1])",
                             "dw_out = dy.reshape(-1, d).T @ np.concatenate([o.reshape(B, S, A), f], axis=-1).reshape(-1, ag.shape[-1])")],
+    "relerr_denominator_from_test": [("denom = np.abs(y_ref).max()", "denom = np.abs(y_test).max()")],
+    "relerr_mean_difference": [("np.abs(y_test - y_ref).max() / denom", "np.abs(y_test - y_ref).mean() / denom")],
+    "relerr_elementwise_ratio": [("np.abs(y_test - y_ref).max() / denom",
+                                  "(np.abs(y_test - y_ref) / np.maximum(np.abs(y_ref), 1e-300)).max()")],
     "dw_in_from_x": [("dw_in = dz.reshape(-1, z.shape[-1]).T @ u.reshape(-1, d)",
                       "dw_in = dz.reshape(-1, z.shape[-1]).T @ x.reshape(-1, d)")],
 }

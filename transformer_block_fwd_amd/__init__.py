@@ -33,6 +33,7 @@ __all__ = [
     "PblockVariant", "PblockVariantWeights", "make_variant", "pblock_forward_variant",
     "PblockGrads", "pblock_train_workspace_bytes", "pblock_forward_train", "pblock_backward",
     "pblock_forward_serial", "pblock_forward_chunked", "pblock_mfma_loop", "as_cfg", "BACKWARD_KERNEL_NAMES",
+    "pblock_activation", "ACTIVATION_FORMS",
 ]
 
 KERNEL_NAMES = ("layernorm", "gemm_in", "attention", "gemm_out")
@@ -295,6 +296,22 @@ def pblock_kernel_times(handle: int, backward: bool = False) -> tuple[dict, int]
     _abi.check(_abi.lib().pblock_kernel_times(ctypes.c_void_p(handle), ms, len(names), ctypes.byref(n)),
                "pblock_kernel_times")
     return dict(zip(names, [float(v) for v in ms])), n.value
+
+
+ACTIVATION_FORMS = {"gelu_erf_f32": _abi.PBLOCK_ACT_GELU_ERF_F32, "gelu_erf_bf16": _abi.PBLOCK_ACT_GELU_ERF_BF16,
+                    "gelu_tanh": _abi.PBLOCK_ACT_GELU_TANH, "gelu_erf_grad": _abi.PBLOCK_ACT_GELU_ERF_GRAD}
+
+
+def pblock_activation(z, out, form: str, stream=None) -> None:
+    """The device GeLU form ``form`` (a key of ACTIVATION_FORMS) of each float32 value of z into out."""
+    n = z.numel()
+    for t, name in ((z, "z"), (out, "out")):
+        if t.dtype.itemsize != 4 or not t.is_floating_point() or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if out.numel() != n:
+        raise ValueError("z and out must have the same number of elements")
+    _abi.check(_abi.lib().pblock_activation(_ptr(z), _ptr(out), int(n), ACTIVATION_FORMS[form], _stream(stream)),
+               "pblock_activation")
 
 
 def pblock_swa_attention(qkv, ld_qkv, o, ld_o, B, S, H, hd, W, dtype="bf16", stream=None) -> None:

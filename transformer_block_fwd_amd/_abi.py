@@ -28,6 +28,12 @@ globals().update({name: code for code, name in STATUS_NAMES.items()})
 PBLOCK_F32 = 0
 PBLOCK_BF16 = 1
 
+# device GeLU forms of pblock_activation
+PBLOCK_ACT_GELU_ERF_F32 = 0
+PBLOCK_ACT_GELU_ERF_BF16 = 1
+PBLOCK_ACT_GELU_TANH = 2
+PBLOCK_ACT_GELU_ERF_GRAD = 3
+
 
 class PblockCfg(ctypes.Structure):
     _fields_ = [
@@ -117,6 +123,7 @@ _SIGNATURES = {
                                         _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
     "pblock_backward": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.POINTER(PblockCfg),
                                    _c.c_void_p, _c.POINTER(PblockGrads), _c.c_void_p, _c.c_int64, _c.c_void_p]),
+    "pblock_activation": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int32, _c.c_void_p]),
     "pblock_forward_chunked": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.POINTER(PblockCfg),
                                           _c.c_void_p, _c.c_int32, _c.POINTER(_c.c_void_p),
                                           _c.POINTER(_c.c_void_p), _c.c_void_p]),

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
   // Copies: instruction c of this wave fills LDS bytes [1024 i, 1024 i + 1024) of a tile,
   // i = wave * NIW + c; lane L writes 16 bytes at 1024 i + 16 L = row r, physical chunk pc,
   // and fetches the row's logical chunk pc ^ swz(r).  Offsets are relative to the tile's
-  // first row; rows past the sequence end are clamped to its last row (masked anyway).
+  // first row; rows past the last query of the launch are clamped to it (masked anyway).
   auto copy_row = [&](int c) { return (1024 * (wave * NIW + c) + 16 * lane) / ROWB; };
   auto copy_pc = [&](int c) { return ((16 * lane) % ROWB) / 16; };
   // (fixed array bounds: the host compiler drops the kernel's launch stub when a lambda
@@ -147,11 +147,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
     koff[c] = uint32_t(r) * ldb + uint32_t((pc ^ swz_k<HD>(r)) << 4);
     voff[c] = uint32_t(r) * ldb + uint32_t((pc ^ swz_v<HD>(r)) << 4);
   }
+  // Key rows at or past q_hi are never attended by this launch's queries (causal), and in a
+  // position-chunked forward they have not been projected yet: rows are clamped to q_hi - 1, so
+  // no stale value (a NaN times a zero weight is NaN) reaches the P V product.
+  const int kv_end = a.q_hi;
   auto issue = [&](int t, uint8_t* ks, uint8_t* vs) {
     const int j0 = t * BKV;
     const uint8_t* kt = kbase + int64_t(j0) * ldb;
     const uint8_t* vt = vbase + int64_t(j0) * ldb;
-    if (j0 + BKV <= S) {
+    if (j0 + BKV <= kv_end) {
 #pragma unroll
       for (int c = 0; c < NIW; ++c) {
         __builtin_amdgcn_global_load_lds(kt + koff[c], (lds_void*)(ks + 1024 * (wave * NIW + c)), 16, 0, 0);
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
 #pragma unroll
       for (int c = 0; c < NIW; ++c) {
         const int r = copy_row(c), pc = copy_pc(c);
-        const uint32_t rb = uint32_t(min(j0 + r, S - 1) - j0) * ldb;
+        const uint32_t rb = uint32_t(min(j0 + r, kv_end - 1) - j0) * ldb;
         __builtin_amdgcn_global_load_lds(kt + rb + uint32_t((pc ^ swz_k<HD>(r)) << 4),
                                          (lds_void*)(ks + 1024 * (wave * NIW + c)), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vt + rb + uint32_t((pc ^ swz_v<HD>(r)) << 4),

@@ -6,7 +6,7 @@
 //                           column partials of du xhat and du;
 //   column_sum_kernel       dgamma, dbeta from those partials.
 // The chain rule through LayerNorm, GeLU and attention is the one the MegaScale guided reading's
-// section 3 implies for the backward pass ("the same is done in the backward pass").
+// section 3 implies for the backward pass (its forward-pass overlap carries over to it).
 #pragma once
 
 #include "common.hpp"

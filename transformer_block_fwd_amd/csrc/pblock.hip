@@ -181,9 +181,25 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(int iters, float* sin
   sink[s] = t;
 }
 
+// The device GeLU forms of the GEMM epilogues, evaluated on their own (test entry):
+// out[i] = f(z[i]) in fp32, before any bf16 rounding.  Grid-stride over n values.
+__global__ __launch_bounds__(256) void activation_kernel(const float* __restrict__ z, float* __restrict__ out,
+                                                         int64_t n, int form) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const float v = z[i];
+    float r;
+    if (form == PBLOCK_ACT_GELU_ERF_F32) r = gelu_erf(v);
+    else if (form == PBLOCK_ACT_GELU_ERF_BF16) r = gelu_erf_bf16out(v);
+    else if (form == PBLOCK_ACT_GELU_TANH) r = gelu_tanh(v);
+    else r = gelu_erf_grad(v);
+    out[i] = r;
+  }
+}
+
 // ------------------------------------------------------------------------ launches
 
 constexpr int64_t kMaxGridWgs = (int64_t(1) << 24) - 1;  // workgroups of 256 in one launch
+constexpr int64_t kMaxAttnLd = int64_t(1) << 24;          // row stride (elements) of the attention entry point
 
 template <typename T>
 void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d, float eps, hipStream_t s,
@@ -264,6 +280,8 @@ void launch_gemm_f32(const GemmArgsF32& g, hipStream_t s) {
 void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, int B, int S, int H, int hd, int W,
                       int dtype, hipStream_t s, int q_lo = 0, int q_hi = -1, float* lse = nullptr) {
   if (q_hi < 0) q_hi = S;
+  // W >= S is full causal attention; clamping keeps every window sum in the kernels' int range
+  W = std::min(W, S);
   const float scale = 1.0f / std::sqrt(float(hd));
   if (dtype == PBLOCK_BF16) {
     AttnArgs a{};
@@ -346,19 +364,14 @@ int drain_events(pblock_s* h) {
   return PBLOCK_OK;
 }
 
-// Argument checks shared by both block forms (all before any launch).
-int check_forward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out, Dims* dm_out) {
-  if (!h) return fail(PBLOCK_ERR_NULL, "handle is NULL");
+// Argument checks of the block forward that need no handle (all before any launch): pointers
+// and cfg (part 1), alignment and aliasing (part 2).
+int check_block_ptrs(const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out) {
   if (!x || !w || !out || !w->ln_gamma || !w->ln_beta || !w->w_in || !w->w_out)
     return fail(PBLOCK_ERR_NULL, "x, out, weights or a weight pointer is NULL");
-  int st = validate(cfg);
-  if (st != PBLOCK_OK) return st;
-  const pblock_cfg& c = *cfg;
-  const pblock_cfg& hc = h->cfg;
-  if (c.d != hc.d || c.H != hc.H || c.hd != hc.hd || c.ffn != hc.ffn || c.dtype != hc.dtype)
-    return fail(PBLOCK_ERR_CFG_MISMATCH, "d, H, hd, ffn and dtype must equal the handle's");
-  const Dims dm = dims(&c);
-  if (dm.M > h->m_cap) return fail(PBLOCK_ERR_CFG_MISMATCH, "B*S exceeds the handle's B*S");
+  return validate(cfg);
+}
+int check_block_layout(const void* x, const pblock_weights* w, const pblock_cfg& c, const Dims& dm, void* out) {
   if (!aligned16(x) || !aligned16(out) || !aligned16(w->ln_gamma) || !aligned16(w->ln_beta) ||
       !aligned16(w->w_in) || !aligned16(w->w_out))
     return fail(PBLOCK_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
@@ -368,6 +381,22 @@ int check_forward(pblock_t h, const void* x, const pblock_weights* w, const pblo
       overlap(out, xb, w->w_out, int64_t(c.d) * dm.k_out * es) || overlap(out, xb, w->ln_gamma, c.d * es) ||
       overlap(out, xb, w->ln_beta, c.d * es))
     return fail(PBLOCK_ERR_ALIAS, "out overlaps x or a weight");
+  return PBLOCK_OK;
+}
+
+// Argument checks shared by the handle's block forms (all before any launch).
+int check_forward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out, Dims* dm_out) {
+  if (!h) return fail(PBLOCK_ERR_NULL, "handle is NULL");
+  int st = check_block_ptrs(x, w, cfg, out);
+  if (st != PBLOCK_OK) return st;
+  const pblock_cfg& c = *cfg;
+  const pblock_cfg& hc = h->cfg;
+  if (c.d != hc.d || c.H != hc.H || c.hd != hc.hd || c.ffn != hc.ffn || c.dtype != hc.dtype)
+    return fail(PBLOCK_ERR_CFG_MISMATCH, "d, H, hd, ffn and dtype must equal the handle's");
+  const Dims dm = dims(&c);
+  if (dm.M > h->m_cap) return fail(PBLOCK_ERR_CFG_MISMATCH, "B*S exceeds the handle's B*S");
+  st = check_block_layout(x, w, c, dm, out);
+  if (st != PBLOCK_OK) return st;
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess || dev != h->device) return fail(PBLOCK_ERR_DEVICE, "current device differs from the handle's");
@@ -568,6 +597,24 @@ int check_train(pblock_t h, const void* x, const pblock_weights* w, const pblock
   return PBLOCK_OK;
 }
 
+// The four launches of the block forward on stream s, intermediates in ws.
+void enqueue_forward(const Ws& ws, const void* x, const pblock_weights* w, const pblock_cfg& c, const Dims& dm,
+                     void* out, hipStream_t s, Timer* tm) {
+  const int64_t A = dm.A;
+  run_layernorm(x, w->ln_gamma, w->ln_beta, ws.u, dm.M, c, s);
+  tm->mark(0);
+  // Z = u W_in^T: Q|K|V columns to QKV, FC1 columns through GeLU to AG[:, A:]
+  run_gemm_in(ws.u, c.d, w->w_in, c.d, dm.M, dm.n_in, c.d, ws.qkv, 3 * A, ws.ag, dm.k_out, A, 3 * A, c.dtype, ws.scr,
+              s);
+  tm->mark(1);
+  launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
+  tm->mark(2);
+  // y = [attention | GeLU] W_out^T (+ x): both branches summed in one accumulator
+  run_gemm_out(ws.ag, dm.k_out, w->w_out, dm.k_out, dm.M, c.d, dm.k_out, out, c.add_residual ? x : nullptr, c.dtype,
+               ws.scr, s);
+  tm->mark(3);
+}
+
 }  // namespace
 
 extern "C" {
@@ -709,26 +756,11 @@ int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pbl
     Dims dm;
     int st = check_forward(h, x, w, cfg, out, &dm);
     if (st != PBLOCK_OK) return st;
-    const pblock_cfg& c = *cfg;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const Ws ws = workspace(h);
     Timer tm;
     st = tm.begin(h, s);
     if (st != PBLOCK_OK) return st;
-    const int64_t A = dm.A;
-
-    run_layernorm(x, w->ln_gamma, w->ln_beta, ws.u, dm.M, c, s);
-    tm.mark(0);
-    // Z = u W_in^T: Q|K|V columns to QKV, FC1 columns through GeLU to AG[:, A:]
-    run_gemm_in(ws.u, c.d, w->w_in, c.d, dm.M, dm.n_in, c.d, ws.qkv, 3 * A, ws.ag, dm.k_out, A, 3 * A, c.dtype, ws.scr,
-                s);
-    tm.mark(1);
-    launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
-    tm.mark(2);
-    // y = [attention | GeLU] W_out^T (+ x): both branches summed in one accumulator
-    run_gemm_out(ws.ag, dm.k_out, w->w_out, dm.k_out, dm.M, c.d, dm.k_out, out, c.add_residual ? x : nullptr, c.dtype,
-                 ws.scr, s);
-    tm.mark(3);
+    enqueue_forward(workspace(h), x, w, *cfg, dm, out, s, &tm);
     h->last_m = dm.M;
     return launch_status("pblock_forward launch");
   } catch (...) {
@@ -1047,7 +1079,8 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
       ab.lse = reinterpret_cast<const float*>(base + T.lse);
       ab.delta = reinterpret_cast<float*>(base + T.delta);
       ab.dqkv = reinterpret_cast<uint16_t*>(base + T.dz); ab.ld_dqkv = dm.n_in;
-      ab.B = c.B; ab.S = c.S; ab.H = c.H; ab.W = c.W;
+      ab.B = c.B; ab.S = c.S; ab.H = c.H;
+      ab.W = std::min(c.W, c.S);  // W >= S is full causal; the dK/dV band sums stay in int range
       ab.scale = 1.0f / std::sqrt(float(c.hd));
       ab.scale_log2 = ab.scale * 1.4426950408889634f;
       const unsigned gq = unsigned(int64_t((c.S + kAttnBQ - 1) / kAttnBQ) * c.B * c.H);
@@ -1132,6 +1165,9 @@ int pblock_swa_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o,
     const int64_t A = int64_t(H) * hd;
     if (ld_qkv < 3 * A || ld_o < A || (ld_qkv % 8) != 0 || (ld_o % 8) != 0)
       return fail(PBLOCK_ERR_SHAPE, "ld_qkv >= 3*H*hd and ld_o >= H*hd, both multiples of 8");
+    // the kernels address a 64-row tile with 32-bit byte offsets from its first row
+    if (ld_qkv > kMaxAttnLd || ld_o > kMaxAttnLd)
+      return fail(PBLOCK_ERR_SHAPE, "ld_qkv and ld_o must be <= 2^24 elements");
     if (!aligned16(qkv) || !aligned16(o)) return fail(PBLOCK_ERR_ALIGN, "qkv and o must be 16-byte aligned");
     const int es = elem_size(dtype);
     const int64_t M = int64_t(B) * S;
@@ -1164,6 +1200,26 @@ const char* pblock_strerror(int code) {
 }
 
 const char* pblock_last_error(void) { return g_last_error.c_str(); }
+
+int pblock_activation(const float* z, float* out, int64_t n, int32_t form, void* stream) {
+  try {
+    if (!z || !out) return fail(PBLOCK_ERR_NULL, "z or out is NULL");
+    if (n < 0 || n > (int64_t(1) << 40)) return fail(PBLOCK_ERR_SHAPE, "n must be in [0, 2^40]");
+    if (form != PBLOCK_ACT_GELU_ERF_F32 && form != PBLOCK_ACT_GELU_ERF_BF16 && form != PBLOCK_ACT_GELU_TANH &&
+        form != PBLOCK_ACT_GELU_ERF_GRAD)
+      return fail(PBLOCK_ERR_ARG, "unknown activation form");
+    if (overlap(z, n * 4, out, n * 4) && z != out) return fail(PBLOCK_ERR_ALIAS, "out partly overlaps z");
+    int st = check_device(nullptr);
+    if (st != PBLOCK_OK) return st;
+    if (n == 0) return PBLOCK_OK;
+    const unsigned grid = unsigned(std::min<int64_t>((n + 255) / 256, 4096));
+    hipLaunchKernelGGL(activation_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), z, out, n,
+                       int(form));
+    return launch_status("pblock_activation launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
 
 int pblock_mfma_loop(int32_t workgroups, int32_t iterations, float* sink, void* stream) {
   try {
