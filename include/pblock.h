@@ -122,6 +122,21 @@ int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle);
 int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg,
                    void* out, void* stream);
 
+/* pblock_forward without a handle and without allocating, for callers that cannot call
+ * hipMalloc: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The intermediates (u, QKV, AG and the GEMM tail partials, laid out as in a
+ * handle's workspace) live in a static device array of 256 MiB that the library holds on every
+ * GPU it runs on until the process ends; its address is looked up once per device on the first
+ * call there.  A cfg whose intermediates need more than 256 MiB gives PBLOCK_ERR_SHAPE (the
+ * 175B shard and the small workload fit; the 8192-token workloads do not).  The same kernels
+ * and launches as pblock_forward, so the results are the same bits.  Calls on one GPU share its
+ * array: calls that overlap in time on one GPU (two streams, two threads) race and give wrong
+ * results; calls on one stream, one after another, are safe.  Nothing in the array needs to
+ * start at zero, so it is never cleared.  Per-kernel timing does not cover this entry point.
+ * x, weights, out and cfg rules as pblock_forward (any B*S up to the 256 MiB limit). */
+int pblock_forward_static(const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out,
+                          void* stream);
+
 /* The standard (serial) layer the parallel block replaces, built from the same
  * kernels for comparison (MegaScale guided reading, section 2: the usual layer
  * is sequential, its feed-forward part taking the attention part's result as

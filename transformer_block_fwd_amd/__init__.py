@@ -33,7 +33,7 @@ __all__ = [
     "PblockVariant", "PblockVariantWeights", "make_variant", "pblock_forward_variant",
     "PblockGrads", "pblock_train_workspace_bytes", "pblock_forward_train", "pblock_backward",
     "pblock_forward_serial", "pblock_forward_chunked", "pblock_mfma_loop", "as_cfg", "BACKWARD_KERNEL_NAMES",
-    "pblock_activation", "ACTIVATION_FORMS",
+    "pblock_activation", "ACTIVATION_FORMS", "pblock_forward_static",
 ]
 
 KERNEL_NAMES = ("layernorm", "gemm_in", "attention", "gemm_out")
@@ -138,6 +138,19 @@ def pblock_forward(handle: int, x, weights, cfg, out, stream=None) -> None:
     w = PblockWeights(_ptr(gamma), _ptr(beta), _ptr(w_in), _ptr(w_out))
     _abi.check(_abi.lib().pblock_forward(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), ctypes.byref(c),
                                          _ptr(out), _stream(stream)), "pblock_forward")
+
+
+def pblock_forward_static(x, weights, cfg, out, stream=None) -> None:
+    """pblock_forward with the library's static device workspace: no handle, no allocation."""
+    c = as_cfg(cfg)
+    gamma, beta, w_in, w_out = weights
+    M, A = c.B * c.S, c.H * c.hd
+    for t, name, n in ((x, "x", M * c.d), (out, "out", M * c.d), (gamma, "ln_gamma", c.d), (beta, "ln_beta", c.d),
+                       (w_in, "w_in", (3 * A + c.ffn) * c.d), (w_out, "w_out", c.d * (A + c.ffn))):
+        _check_tensor(t, name, c.dtype, n)
+    w = PblockWeights(_ptr(gamma), _ptr(beta), _ptr(w_in), _ptr(w_out))
+    _abi.check(_abi.lib().pblock_forward_static(_ptr(x), ctypes.byref(w), ctypes.byref(c), _ptr(out), _stream(stream)),
+               "pblock_forward_static")
 
 
 def pblock_forward_serial(handle: int, x, weights, ln2, cfg, out, stream=None) -> None:

@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -597,6 +598,43 @@ int check_train(pblock_t h, const void* x, const pblock_weights* w, const pblock
   return PBLOCK_OK;
 }
 
+// ------------------------------------------------------------------------ static workspace
+// The no-allocation forward keeps its intermediates in this file-scope device array: one copy
+// per GPU the library runs on, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (in host code it names a host-side stand-in); it uses the device address
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr int64_t kStaticScratchBytes = int64_t(256) << 20;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch` per device (nullptr: not looked up yet)
+int g_scratch_cus[64];    // compute units of that device
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+int static_scratch(int dev, void** ptr, int* n_cu) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(PBLOCK_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus <= 0) return fail(PBLOCK_ERR_DEVICE, "cannot query the compute-unit count");
+    g_scratch_cus[dev] = cus;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *n_cu = g_scratch_cus[dev];
+  return PBLOCK_OK;
+}
+
 // The four launches of the block forward on stream s, intermediates in ws.
 void enqueue_forward(const Ws& ws, const void* x, const pblock_weights* w, const pblock_cfg& c, const Dims& dm,
                      void* out, hipStream_t s, Timer* tm) {
@@ -763,6 +801,41 @@ int pblock_forward(pblock_t h, const void* x, const pblock_weights* w, const pbl
     enqueue_forward(workspace(h), x, w, *cfg, dm, out, s, &tm);
     h->last_m = dm.M;
     return launch_status("pblock_forward launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int pblock_forward_static(const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out, void* stream) {
+  try {
+    int st = check_block_ptrs(x, w, cfg, out);
+    if (st != PBLOCK_OK) return st;
+    const pblock_cfg& c = *cfg;
+    const Dims dm = dims(&c);
+    st = check_block_layout(x, w, c, dm, out);
+    if (st != PBLOCK_OK) return st;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st != PBLOCK_OK) return st;
+    void* base = nullptr;
+    int n_cu = 0;
+    st = static_scratch(dev, &base, &n_cu);
+    if (st != PBLOCK_OK) return st;
+    const WsLayout lay = ws_layout(&c, n_cu);
+    if (lay.rope > kStaticScratchBytes)
+      return fail(PBLOCK_ERR_SHAPE, "cfg needs " + std::to_string(lay.rope) + " bytes of workspace; the static one holds " +
+                                        std::to_string(kStaticScratchBytes));
+    char* b = static_cast<char*>(base);
+    Ws ws;
+    ws.u = b + lay.u;
+    ws.qkv = b + lay.qkv;
+    ws.ag = b + lay.ag;
+    ws.rope = nullptr;
+    ws.scr.partials = reinterpret_cast<float*>(b + lay.partials);
+    ws.scr.G = n_cu;
+    Timer tm;  // no timing: no handle
+    enqueue_forward(ws, x, w, c, dm, out, static_cast<hipStream_t>(stream), &tm);
+    return launch_status("pblock_forward_static launch");
   } catch (...) {
     return fail(PBLOCK_ERR_ARG, "internal error");
   }
