@@ -69,6 +69,10 @@ def parse():
     p.add_argument("--chunk-input", action="store_true",
                    help="with --chunks: pass per-chunk input events too (all steps chunked, the all-gather side "
                         "of the overlap); without it only the output GEMM is chunked")
+    p.add_argument("--rowchunks", action="store_true",
+                   help="with --chunks: one output-GEMM launch that publishes each chunk through a device flag "
+                        "(pblock_forward_rowchunks) instead of one launch per chunk; one more step with the "
+                        "consumer (pblock_pack_chunks) on a second stream reports the publication times")
     p.add_argument("--gelu-tanh", action="store_true", help="variant: tanh-form GeLU")
     p.add_argument("--bias", action="store_true", help="variant: biases on both projections")
     p.add_argument("--rope", type=float, default=0.0, metavar="BASE",
@@ -298,6 +302,10 @@ def main():
     ready = [None] * args.chunks if args.chunk_input else None
     if args.chunk_input and not args.chunks:
         raise SystemExit("--chunk-input needs --chunks")
+    if args.rowchunks and (not args.chunks or args.chunk_input or cfg.dtype != "bf16"):
+        raise SystemExit("--rowchunks needs --chunks (whole input, bf16)")
+    flags = torch.zeros(max(args.chunks, 1), dtype=torch.int32, device="cuda")
+    epoch = [0]
     train_dy = None
     if args.train:
         if args.block != "parallel" or use_variant or args.chunks or cfg.dtype != "bf16":
@@ -318,6 +326,9 @@ def main():
             tb.pblock_forward_serial(h, dev["x"], weights, (dev["gamma2"], dev["beta2"]), cfg, out, stream)
         elif use_variant:
             tb.pblock_forward_variant(h, dev["x"], weights, extra, cfg, variant, out, stream)
+        elif chunked and args.rowchunks:
+            epoch[0] = epoch[0] % 0x7FFFFFFF + 1
+            tb.pblock_forward_rowchunks(h, dev["x"], weights, cfg, out, args.chunks, flags, epoch[0], stream)
         elif chunked:
             tb.pblock_forward_chunked(h, dev["x"], weights, cfg, out, args.chunks, ready, done, stream)
         else:
@@ -348,11 +359,9 @@ def main():
           flush=True)
 
     chunking = None
+    published_us = None
     if args.chunks:
-        # completion of each chunk's rows of out within the last timed step
-        t_done = [marks[-2].elapsed_time(e) for e in done]
-        # the same forward unchunked, with per-kernel timing, for the kernel and roofline figures
-        tb.pblock_set_timing(h, True)
+        # the same forward unchunked, untimed per kernel, for the ratio
         u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         n_un = max(5, args.steps // 3)
         u0.record(stream)
@@ -360,14 +369,47 @@ def main():
             step(chunked=False)
         u1.record(stream)
         torch.cuda.synchronize()
+        unchunked = u0.elapsed_time(u1) / n_un
+    if args.rowchunks:
+        # one more step with the consumer on a second stream: when each chunk's flag was seen
+        send = torch.empty_like(out)
+        stamps = torch.zeros(args.chunks, dtype=torch.int64, device="cuda")
+        from transformer_block_fwd_amd.streams import cu_masked_stream, destroy_stream
+
+        n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+        side = cu_masked_stream(n_cus - 32, 32, n_cus)  # a hardware queue of its own, the last 32 CUs
+        prod = torch.cuda.Stream()  # not the null stream, which would wait for the consumer
+        torch.cuda.synchronize()
+        epoch[0] = epoch[0] % 0x7FFFFFFF + 1
+        tb.pblock_pack_chunks(out, cfg, args.chunks, flags, epoch[0], send, stamps, side)
+        tb.pblock_forward_rowchunks(h, dev["x"], weights, cfg, out, args.chunks, flags, epoch[0], prod)
+        torch.cuda.synchronize()
+        destroy_stream(side)
+        st = [int(v) & 0xFFFFFFFFFFFFFFFF for v in stamps.cpu().tolist()]
+        if any(v == 0xFFFFFFFFFFFFFFFF for v in st):
+            print("[bench] the consumer timed out waiting for a chunk", file=sys.stderr, flush=True)
+        else:
+            published_us = [round((v - min(st)) / 100.0, 2) for v in st]  # 100 MHz device clock
+            print(f"[bench] chunk publication (us after the first): {published_us}", file=sys.stderr, flush=True)
+    if args.chunks:
+        # completion of each chunk's rows of out within the last timed step
+        t_done = [marks[-2].elapsed_time(e) for e in done] if not args.rowchunks else None
+        # the same forward unchunked, with per-kernel timing, for the kernel and roofline figures
+        tb.pblock_set_timing(h, True)
+        for _ in range(max(5, args.steps // 3)):
+            step(chunked=False)
+        torch.cuda.synchronize()
         kernel_ms, n_fwd = tb.pblock_kernel_times(h)
         tb.pblock_set_timing(h, False)
-        unchunked = u0.elapsed_time(u1) / n_un
-        chunking = {"chunks": args.chunks, "input_chunked": bool(args.chunk_input), "chunk_done_ms": [round(v, 5) for v in t_done],
+        chunking = {"chunks": args.chunks, "input_chunked": bool(args.chunk_input),
+                    "form": "one output-GEMM launch, flags" if args.rowchunks else "one launch per chunk, events",
+                    "chunk_done_ms": [round(v, 5) for v in t_done] if t_done else None,
+                    "published_us_after_first": published_us,
                     "unchunked_ms_per_step": round(unchunked, 5),
                     "chunked_over_unchunked": round((ms_total / args.steps) / unchunked, 4)}
-        print(f"[bench] chunk completion (ms into the step): {[round(v, 3) for v in t_done]}", file=sys.stderr,
-              flush=True)
+        if t_done:
+            print(f"[bench] chunk completion (ms into the step): {[round(v, 3) for v in t_done]}", file=sys.stderr,
+                  flush=True)
 
     cold = None
     if args.cold_steps > 0:

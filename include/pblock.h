@@ -179,6 +179,46 @@ int pblock_forward_chunked(pblock_t h, const void* x, const pblock_weights* w, c
                            void* out, int32_t n_chunks, void* const* ready_events, void* const* done_events,
                            void* stream);
 
+/* The block forward with its output published chunk by chunk from inside one output-GEMM
+ * launch, for overlapping the reduce-scatter of tensor/sequence parallelism with the rest of
+ * the GEMM (MegaScale guided reading, section 3: the GEMM next to the collective is cut into
+ * chunks so that one chunk's communication overlaps the next chunk's computation).  Chunk k
+ * holds positions [floor(k*S/n), floor((k+1)*S/n)) of every sequence, n = n_chunks.
+ * LayerNorm, the fused QKV+FC1 GEMM and attention run once over every row; the output GEMM
+ * (+ residual) then runs its tiles in chunk order (rows of earlier chunks first) as whole
+ * waves of 256x256 tiles plus, for a remainder of at most half a wave, 128x256 half-height
+ * tiles, with no k-split.  When the last tile touching chunk k has stored its rows, they are
+ * written back for the whole device and flags[k] is set to `epoch` (a release store at
+ * device scope): a kernel on another stream that reads flags[k] == epoch with acquire
+ * semantics (pblock_pack_chunks does) then reads the final rows of chunk k.
+ *   flags    [n_chunks] uint32, caller-owned device memory, 4-byte aligned; the library only
+ *            stores epoch into it.  Start it at 0 (or any value other than the first epoch).
+ *   epoch    nonzero, and different from the previous call's so that a consumer cannot take
+ *            an earlier call's flag for this one's (e.g. a step counter).
+ * 1 <= n_chunks <= min(S, 64) (PBLOCK_ERR_ARG); bf16 only (PBLOCK_ERR_DTYPE); flags must not
+ * overlap out, x or a weight (PBLOCK_ERR_ALIAS).  The handle keeps one tile counter per chunk
+ * (zeroed at creation, reset by each chunk's last tile), so a handle must not run two of these
+ * calls at once.  The result equals pblock_forward's up to floating-point summation order.
+ * Other rules, and per-kernel timing, as pblock_forward. */
+int pblock_forward_rowchunks(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg,
+                             void* out, int32_t n_chunks, uint32_t* flags, uint32_t epoch, void* stream);
+
+/* The consumer side of pblock_forward_rowchunks (the local half of a reduce-scatter): for each
+ * chunk k, waits until flags[k] == epoch, then copies chunk k's rows of out (bf16 [B, S, d])
+ * into piece k of send, the rows rank k of a reduce-scatter receives: piece k starts at
+ * element B*floor(k*S/n)*d and holds the chunk's rows sequence by sequence.  stamps[k]
+ * receives the device real-time clock (100 MHz) at the moment the flag was seen.  Each wait is
+ * bounded: after 2 s without the flag, stamps[k] = UINT64_MAX and piece k is not written (the
+ * kernel always ends).  Run it on a stream other than the producer's, enqueued before the
+ * producer's work, so that it consumes chunks while the output GEMM still runs.
+ *   out, send   bf16, B*S*d elements each, 16-byte aligned; flags [n_chunks] uint32, 4-byte
+ *               aligned; stamps [n_chunks] uint64, 8-byte aligned; all device memory owned by
+ *               the caller, none overlapping another.
+ * cfg gives B, S, d (its other fields are validated as usual); bf16 only; n_chunks as
+ * pblock_forward_rowchunks.  Enqueued on `stream`, no sync. */
+int pblock_pack_chunks(const void* out, const pblock_cfg* cfg, int32_t n_chunks, const uint32_t* flags,
+                       uint32_t epoch, void* send, uint64_t* stamps, void* stream);
+
 /* Switches for the choices the pages leave open (MegaScale guided reading: section 2
  * names the block's shape but no positional encoding, bias or normalisation layout;
  * section 4 names GeLU without its form).  All zero = pblock_forward.

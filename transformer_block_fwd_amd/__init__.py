@@ -33,7 +33,8 @@ __all__ = [
     "PblockVariant", "PblockVariantWeights", "make_variant", "pblock_forward_variant",
     "PblockGrads", "pblock_train_workspace_bytes", "pblock_forward_train", "pblock_backward",
     "pblock_forward_serial", "pblock_forward_chunked", "pblock_mfma_loop", "as_cfg", "BACKWARD_KERNEL_NAMES",
-    "pblock_activation", "ACTIVATION_FORMS", "pblock_forward_static",
+    "pblock_activation", "ACTIVATION_FORMS", "pblock_forward_static", "pblock_forward_rowchunks",
+    "pblock_pack_chunks",
 ]
 
 KERNEL_NAMES = ("layernorm", "gemm_in", "attention", "gemm_out")
@@ -273,6 +274,41 @@ def pblock_forward_chunked(handle: int, x, weights, cfg, out, n_chunks: int, rea
     _abi.check(_abi.lib().pblock_forward_chunked(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), ctypes.byref(c),
                                                  _ptr(out), int(n_chunks), ready, done, _stream(stream)),
                "pblock_forward_chunked")
+
+
+def pblock_forward_rowchunks(handle: int, x, weights, cfg, out, n_chunks: int, flags, epoch: int,
+                             stream=None) -> None:
+    """The forward with its output published chunk by chunk: flags (int32/uint32 GPU tensor of
+    n_chunks) gets epoch at chunk k's entry once its rows of out are final."""
+    c = as_cfg(cfg)
+    gamma, beta, w_in, w_out = weights
+    M, A = c.B * c.S, c.H * c.hd
+    for t, name, n in ((x, "x", M * c.d), (out, "out", M * c.d), (gamma, "ln_gamma", c.d), (beta, "ln_beta", c.d),
+                       (w_in, "w_in", (3 * A + c.ffn) * c.d), (w_out, "w_out", c.d * (A + c.ffn))):
+        _check_tensor(t, name, c.dtype, n)
+    _check_words(flags, "flags", 4, n_chunks)
+    w = PblockWeights(_ptr(gamma), _ptr(beta), _ptr(w_in), _ptr(w_out))
+    _abi.check(_abi.lib().pblock_forward_rowchunks(ctypes.c_void_p(handle), _ptr(x), ctypes.byref(w), ctypes.byref(c),
+                                                   _ptr(out), int(n_chunks), _ptr(flags), int(epoch),
+                                                   _stream(stream)), "pblock_forward_rowchunks")
+
+
+def pblock_pack_chunks(out, cfg, n_chunks: int, flags, epoch: int, send, stamps, stream=None) -> None:
+    """Copies each published chunk of out into its piece of send (see the header); stamps is an
+    int64/uint64 GPU tensor of n_chunks receiving the device clock at each publication."""
+    c = as_cfg(cfg)
+    n = c.B * c.S * c.d
+    for t, name in ((out, "out"), (send, "send")):
+        _check_tensor(t, name, c.dtype, n)
+    _check_words(flags, "flags", 4, n_chunks)
+    _check_words(stamps, "stamps", 8, n_chunks)
+    _abi.check(_abi.lib().pblock_pack_chunks(_ptr(out), ctypes.byref(c), int(n_chunks), _ptr(flags), int(epoch),
+                                             _ptr(send), _ptr(stamps), _stream(stream)), "pblock_pack_chunks")
+
+
+def _check_words(t, name, itemsize, n):
+    if not t.is_cuda or not t.is_contiguous() or t.dtype.itemsize != itemsize or t.numel() < n:
+        raise ValueError(f"{name} must be a contiguous GPU tensor of {itemsize}-byte words with >= {n} elements")
 
 
 def pblock_mfma_loop(workgroups: int, iterations: int, sink, stream=None) -> None:

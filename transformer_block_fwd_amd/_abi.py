@@ -125,6 +125,11 @@ _SIGNATURES = {
                                    _c.c_void_p, _c.POINTER(PblockGrads), _c.c_void_p, _c.c_int64, _c.c_void_p]),
     "pblock_forward_static": (_c.c_int, [_c.c_void_p, _c.POINTER(PblockWeights), _c.POINTER(PblockCfg), _c.c_void_p,
                                          _c.c_void_p]),
+    "pblock_forward_rowchunks": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights),
+                                            _c.POINTER(PblockCfg), _c.c_void_p, _c.c_int32, _c.c_void_p,
+                                            _c.c_uint32, _c.c_void_p]),
+    "pblock_pack_chunks": (_c.c_int, [_c.c_void_p, _c.POINTER(PblockCfg), _c.c_int32, _c.c_void_p, _c.c_uint32,
+                                      _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "pblock_activation": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int32, _c.c_void_p]),
     "pblock_forward_chunked": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.POINTER(PblockCfg),
                                           _c.c_void_p, _c.c_int32, _c.POINTER(_c.c_void_p),

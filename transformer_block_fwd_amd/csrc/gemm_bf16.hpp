@@ -40,6 +40,11 @@
 // order with coalesced reads (bitwise deterministic, no atomics, no
 // cross-workgroup fences) and applies the epilogue.
 //
+// When whole waves come first and the remainder would be cut in two k-chunks (between a
+// third and a half of a wave of tiles), it runs instead as twice as many 128 x 256
+// half-height tiles in a second launch of the BM = 128 form: one wave, every tile whole,
+// no partials.
+//
 // L2 locality: workgroup ids are remapped so each XCD (id mod 8) owns a
 // contiguous run of work units, and units are ordered in groups of 8 M-tiles
 // (M fastest): the 32 workgroups an XCD runs at once cover an 8 (M) x 4 (N)
@@ -108,9 +113,66 @@ struct GemmSched {
   int dp_units;     // tiles computed whole (whole waves, or all tiles when a split would be 1)
   int tail;         // tiles computed in k-chunks
   int split;        // k-chunks per tail tile
+  int unit_base;    // half-height launch: unit u is half u % 2 of 256-row tile unit_base + u / 2
+  int wave_units;   // publishing launches: workgroups resident at once (one wave)
 };
 
 constexpr int kGroupM = 8;
+
+// Publication of finished row chunks by the output GEMM (position-chunked forward).  Chunk k
+// holds positions [floor(k S / n), floor((k+1) S / n)) of every sequence; a row r is position
+// r % S of sequence r / S.  Tiles run in publication order (rows of earlier chunks first);
+// every tile that finishes adds one to the counter of each chunk its rows touch, and the tile
+// that brings counter k to need[k] (the number of tiles touching chunk k in this launch pair)
+// resets the counter and sets flags[k] = epoch with release semantics at device scope.
+constexpr int kMaxChunks = 64;
+struct RowPublish {
+  uint32_t* counters;  // [n] zero between calls (the last tile of a chunk resets its counter)
+  uint32_t* flags;     // [n] caller's flags
+  uint32_t epoch;
+  int n;               // chunks, 1 .. kMaxChunks
+  int S;               // positions per sequence
+  int B;               // sequences: M-tiles run position-major over them when S % 256 == 0
+  int group_m;         // M-tiles per group of the publication order (M fastest inside a group)
+  uint32_t need[kMaxChunks];
+};
+
+// Chunk of position p (0 <= p < S) among n chunks: the k with floor(k S / n) <= p < floor((k+1) S / n).
+__host__ __device__ __forceinline__ int chunk_of(int p, int S, int n) {
+  return int((int64_t(p + 1) * n - 1) / S);
+}
+// Bit k set iff some row in [r0, r1) lies in chunk k.
+__host__ __device__ __forceinline__ uint64_t chunk_mask(int r0, int r1, int S, int n) {
+  uint64_t mask = 0;
+  for (int r = r0; r < r1;) {
+    const int b = r / S;
+    const int end = min((b + 1) * S, r1);
+    const int ka = chunk_of(r - b * S, S, n), kb = chunk_of(end - 1 - b * S, S, n);
+    const uint64_t upto = kb >= 63 ? ~uint64_t(0) : ((uint64_t(1) << (kb + 1)) - 1);
+    mask |= upto & ~((uint64_t(1) << ka) - 1);
+    r = end;
+  }
+  return mask;
+}
+// 256-row tile coordinates of tile index L in publication order: groups of group_m M-tiles
+// (in position-major order over the sequences when whole tiles hold one sequence each), M
+// fastest inside a group.
+__host__ __device__ __forceinline__ void tile_coords_pub(int L, int tiles_m, int tiles_n, const RowPublish& pub,
+                                                         int* tm, int* tn) {
+  const int gm = pub.group_m;
+  const int group = gm * tiles_n;
+  const int first = (L / group) * gm;
+  const int gsz = min(tiles_m - first, gm);
+  const int r = L % group;
+  const int im = first + r % gsz;
+  *tn = r / gsz;
+  if (pub.B > 1 && pub.S % 256 == 0) {
+    const int per_seq = pub.S / 256;
+    *tm = (im % pub.B) * per_seq + im / pub.B;
+  } else {
+    *tm = im;
+  }
+}
 
 // Contiguous-per-XCD renumbering of workgroup ids 0 .. n-1 (id mod 8 picks the XCD).
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
@@ -204,10 +266,15 @@ __device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f3
   *reinterpret_cast<u32x4*>(dst) = o;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, GemmSched sk) {
-  constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, NT = kGemmThreads;
-  constexpr int FM = 4, FN = 4;  // 32x32 MFMA tiles per wavefront (128 x 128)
+template <int EPI, int BM = kGemmBM, bool PUB = false>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, GemmSched sk, RowPublish pub) {
+  static_assert(BM == 256 || BM == 128, "tile height 256 or 128");
+  constexpr int BN = kGemmBN, BK = kGemmBK, NT = kGemmThreads;
+  constexpr int FM = BM / 64, FN = 4;  // 32x32 MFMA tiles per wavefront (BM/2 x 128)
+  constexpr int NA = BM / 32;          // A copy instructions per wavefront and slab (B: 8)
+  // copy instructions of slab t+2 issued in k-steps 1, 2 and 3 (A then B counts)
+  constexpr int CA1 = NA < 3 ? NA : 3, CA2 = (NA < 5 ? NA : 5) - CA1, CA3 = NA - CA1 - CA2;
+  constexpr int C1 = CA1 + 3, C2 = CA2 + 2, C3 = CA3 + 3;
   __shared__ __attribute__((aligned(1024))) uint16_t a0[kGemmHalf];
   __shared__ __attribute__((aligned(1024))) uint16_t b0[kGemmHalf];
   __shared__ __attribute__((aligned(1024))) uint16_t a1[kGemmHalf];
@@ -220,7 +287,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   const int lr = lane & 31, lg = lane >> 5;
 
   int L, kb, ke, tl = -1, chunk = 0;
-  if (int(blockIdx.x) < sk.dp_units) {
+  if (PUB) {
+    // publication order wave by wave: wave w runs units [wG, wG + G), each XCD a contiguous run
+    const int G = sk.wave_units;
+    const int w0 = (int(blockIdx.x) / G) * G;
+    L = w0 + xcd_remap(int(blockIdx.x) - w0, min(G, sk.dp_units - w0));
+    kb = 0;
+    ke = sk.KT;
+  } else if (int(blockIdx.x) < sk.dp_units) {
     L = xcd_remap(blockIdx.x, sk.dp_units);
     kb = 0;
     ke = sk.KT;
@@ -234,7 +308,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     ke = int((int64_t(chunk + 1) * sk.KT) / sk.split);
   }
   int tm, tn;
-  tile_coords(L, sk.tiles_m, sk.tiles_n, &tm, &tn);
+  if constexpr (BM == 128) {
+    // half-height tiles of the 256 x 256 tiling (tiles_m counts 256-row tiles)
+    if (PUB) tile_coords_pub(sk.unit_base + L / 2, sk.tiles_m, sk.tiles_n, pub, &tm, &tn);
+    else tile_coords(sk.unit_base + L / 2, sk.tiles_m, sk.tiles_n, &tm, &tn);
+    tm = 2 * tm + (L & 1);
+  } else {
+    if (PUB) tile_coords_pub(L, sk.tiles_m, sk.tiles_n, pub, &tm, &tn);
+    else tile_coords(L, sk.tiles_m, sk.tiles_n, &tm, &tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Copies: instruction i (0..7) of wave w fills 1 KiB block 8w + i of each operand tile =
@@ -248,14 +330,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     offa[p] = uint32_t(lane >> 3) * lda_b + uint32_t(lc << 4);
     offb[p] = uint32_t(lane >> 3) * ldb_b + uint32_t(lc << 4);
   }
-  const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(g.a) + int64_t(m0 + wave * 64) * lda_b;
-  // copy instructions i0 .. i1-1 (one A and one B instruction each) of slab kt
+  // A: wave w's NA instructions fill rows w*BM/4 .. +BM/4 (1 KiB block w*NA + i = rows
+  // w*BM/4 + 8i + l/8: the same row swizzle, since BM/4 is a multiple of 16)
+  const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(g.a) + int64_t(m0 + wave * (BM / 4)) * lda_b;
+  // copy instructions i0 .. i1-1 (an A instruction for i < NA, a B instruction each) of slab kt
   auto issue = [&](int kt, uint16_t* sa, uint16_t* sb, int i0, int i1) __attribute__((always_inline)) {
     const uint32_t kofs = uint32_t(kt) * (BK * 2);
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      __builtin_amdgcn_global_load_lds(a_blk + int64_t(8 * i) * lda_b + kofs + offa[i & 1],
-                                       (PBLK_LDS void*)(sa + (wave * 8 + i) * 512), 16, 0, 0);
+      if (i < NA)
+        __builtin_amdgcn_global_load_lds(a_blk + int64_t(8 * i) * lda_b + kofs + offa[i & 1],
+                                         (PBLK_LDS void*)(sa + (wave * NA + i) * 512), 16, 0, 0);
       const int brow = min(n0 + wave * 64 + 8 * i, g.N - 8);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(g.b) + int64_t(brow) * ldb_b + kofs + offb[i & 1],
                                        (PBLK_LDS void*)(sb + (wave * 8 + i) * 512), 16, 0, 0);
@@ -268,7 +353,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const uint32_t o = uint32_t(lr * 128 + (((2 * kk + lg) ^ ((lr >> 1) & 7)) << 4));
-    rda[kk] = o + uint32_t(wm * 128 * 128);
+    rda[kk] = o + uint32_t(wm * (BM / 2) * 128);
     rdb[kk] = o + uint32_t(wn * 128 * 128);
   }
 
@@ -334,24 +419,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     lds_barrier();  // everyone's: the stage is free
     issue(tc, wa, wb, 0, 3);
     mm(1);
-    interleave_cp(6, 0);
+    interleave_cp(C1, 0);
     __builtin_amdgcn_sched_barrier(0);
     issue(tc, wa, wb, 3, 5);
     mm(2);
-    interleave_cp(4, 0);
+    interleave_cp(C2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm_lgkm0<10>();  // own copies of slab t+1 landed (10 of slab t+2 may be in flight)
-    lds_barrier();        // everyone's: slab t+1 is complete
+    wait_vm_lgkm0<C1 + C2>();  // own copies of slab t+1 landed (those of slab t+2 may be in flight)
+    lds_barrier();             // everyone's: slab t+1 is complete
     issue(tc, wa, wb, 5, 8);
     rd(0, na, nb, 0);
     mm(3);
-    interleave_cp(6, 8);
+    interleave_cp(C3, 8);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   issue(kb, a0, b0, 0, 8);
   issue(min(kb + 1, ke - 1), a1, b1, 0, 8);
-  wait_vm_lgkm0<16>();  // slab kb landed
+  wait_vm_lgkm0<NA + 8>();  // slab kb landed
   lds_barrier();
   rd(0, a0, b0, 0);
   const int n = ke - kb;
@@ -363,7 +448,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   if (n & 1) slab(kt, a0, b0, a1, b1);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no copy may still be writing this workgroup's LDS
 
-  // Epilogue through LDS, four rounds: in round i every wave stages its rows wm*128 + i*32 +
+  // Epilogue through LDS, FM rounds: in round i every wave stages its rows wm*BM/2 + i*32 +
   // 0..31 as fp32 (stage pair i&1, the wm half in its own array, 16-byte chunks XOR-permuted
   // by row), then all threads store 64 full rows: bf16 outputs with 16-byte writes, or, for a
   // split-K chunk, its fp32 partial tile (row-major 256 x 256) with 32-byte writes.  Lane
@@ -390,13 +475,32 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       const int c0 = (tid & 31) * 2;
       const f32x4 lo = *reinterpret_cast<const f32x4*>(src + lrow * 256 + ((c0 ^ (lrow & 15)) << 2));
       const f32x4 hi = *reinterpret_cast<const f32x4*>(src + lrow * 256 + (((c0 + 1) ^ (lrow & 15)) << 2));
-      const int ml = half * 128 + i * 32 + lrow, nl = (tid & 31) * 8;
+      const int ml = half * (BM / 2) + i * 32 + lrow, nl = (tid & 31) * 8;
       if (part != nullptr) {
         f32x4* dst = reinterpret_cast<f32x4*>(part + ml * BN + nl);
         dst[0] = lo;
         dst[1] = hi;
       } else if (m0 + ml < g.M && n0 + nl < g.N) {
         store_chunk8<EPI>(g, m0 + ml, n0 + nl, lo, hi);
+      }
+    }
+  }
+  if constexpr (PUB) {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // this thread's stores of the tile are done
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the tile's rows, written back
+      uint64_t mask = chunk_mask(m0, min(m0 + BM, g.M), pub.S, pub.n);
+      while (mask != 0) {
+        const int k = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const uint32_t old = __hip_atomic_fetch_add(pub.counters + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old + 1 == pub.need[k]) {
+          // the chunk's last tile: every other tile's release precedes its increment
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          __hip_atomic_store(pub.counters + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(pub.flags + k, pub.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }

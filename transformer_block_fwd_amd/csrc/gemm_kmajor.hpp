@@ -242,6 +242,8 @@ template <int EPI, bool AK>
 void launch_gemm_kmajor(const GemmArgs& g, float* partials, int G, hipStream_t s) {
   GemmSched sk;
   sk.partials = partials;
+  sk.unit_base = 0;
+  sk.wave_units = G;
   sk.tiles_m = int((g.M + kGemmBM - 1) / kGemmBM);
   sk.tiles_n = int((g.N + kGemmBN - 1) / kGemmBN);
   sk.KT = g.K / kGemmBK;

@@ -31,6 +31,7 @@
 #include "gemm_f32.hpp"
 #include "gemm_kmajor.hpp"
 #include "layernorm.hpp"
+#include "rowchunks.hpp"
 
 using namespace pblk;
 
@@ -79,7 +80,7 @@ int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
 
 struct WsLayout {
-  int64_t u, qkv, ag, partials, rope, total;
+  int64_t u, qkv, ag, partials, rope, counters, total;
 };
 // G = persistent GEMM workgroups (the device's CU count); 0 for a host-only estimate at 256.
 WsLayout ws_layout(const pblock_cfg* c, int G) {
@@ -102,7 +103,9 @@ WsLayout ws_layout(const pblock_cfg* c, int G) {
   }
   w.rope = w.partials + align256(part_bytes);
   // rotary-embedding table: (cos, sin) fp32 for hd/2 pairs at positions 0 .. M-1 (any S <= M)
-  w.total = w.rope + align256(dm.M * c->hd * 4);
+  w.counters = w.rope + align256(dm.M * c->hd * 4);
+  // per-chunk tile counters of the row-chunk publication (zeroed at creation)
+  w.total = w.counters + align256(kMaxChunks * 4);
   return w;
 }
 
@@ -201,6 +204,7 @@ __global__ __launch_bounds__(256) void activation_kernel(const float* __restrict
 
 constexpr int64_t kMaxGridWgs = (int64_t(1) << 24) - 1;  // workgroups of 256 in one launch
 constexpr int64_t kMaxAttnLd = int64_t(1) << 24;          // row stride (elements) of the attention entry point
+constexpr unsigned long long kPackTimeoutTicks = 200000000ull;  // 2 s of the 100 MHz device real-time clock
 
 template <typename T>
 void launch_layernorm(const T* x, const T* g, const T* b, T* u, int64_t M, int d, float eps, hipStream_t s,
@@ -258,17 +262,79 @@ template <int EPI>
 void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s) {
   GemmSched sk;
   sk.partials = scr.partials;
+  sk.wave_units = scr.G;
   sk.tiles_m = int((g.M + kGemmBM - 1) / kGemmBM);
   sk.tiles_n = int((g.N + kGemmBN - 1) / kGemmBN);
   sk.KT = g.K / kGemmBK;
+  sk.unit_base = 0;
   const Split p = plan_split(int64_t(sk.tiles_m) * sk.tiles_n, sk.KT, scr.G);
+  if (p.tail > 0 && p.split == 2 && p.dp_units > 0) {
+    // after whole waves, the remainder as 2 * tail half-height tiles (at most one wave): whole
+    // tiles, no partials, no reduce (measured: 5% off the 4096 x 14336 x 2048 input GEMM, 1.3%
+    // off the 2048 x 12288 x 7680 output GEMM; a GEMM that is one partial wave in all keeps the
+    // k-split, whose halved k loops are faster there)
+    sk.dp_units = p.dp_units;
+    sk.tail = 0;
+    sk.split = 1;
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(unsigned(p.dp_units)), dim3(kGemmThreads), 0, s, g, sk, RowPublish{});
+    GemmSched sh = sk;
+    sh.dp_units = 2 * p.tail;
+    sh.unit_base = p.dp_units;
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 128>), dim3(unsigned(sh.dp_units)), dim3(kGemmThreads), 0, s, g, sh,
+                       RowPublish{});
+    return;
+  }
   sk.dp_units = p.dp_units;
   sk.tail = p.tail;
   sk.split = p.split;
   const unsigned grid = unsigned(p.dp_units + p.tail * p.split);
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk, RowPublish{});
   if (p.tail > 0)
     hipLaunchKernelGGL((gemm_bf16_tail_reduce_kernel<EPI>), dim3(unsigned(p.tail * 32)), dim3(256), 0, s, g, sk);
+}
+
+// The output GEMM with row-chunk publication (pub.n, S, B, flags, counters, epoch set by the
+// caller): tiles in publication order, whole waves of 256 x 256 tiles, then a remainder of at
+// most half a wave as 128 x 256 half-height tiles (no k-split: every tile publishes itself).
+template <int EPI>
+void launch_gemm_bf16_publish(const GemmArgs& g, const SkScratch& scr, RowPublish pub, hipStream_t s) {
+  GemmSched sk{};
+  sk.partials = nullptr;
+  sk.tiles_m = int((g.M + kGemmBM - 1) / kGemmBM);
+  sk.tiles_n = int((g.N + kGemmBN - 1) / kGemmBN);
+  sk.KT = g.K / kGemmBK;
+  sk.split = 1;
+  sk.wave_units = scr.G;
+  const int64_t T = int64_t(sk.tiles_m) * sk.tiles_n;
+  const int64_t dp = (T / scr.G) * scr.G, tail = T - dp;
+  const bool halves = tail > 0 && 2 * tail <= scr.G;
+  const int64_t whole = halves ? dp : T;
+  // tiles touching each chunk, unit by unit as the kernels will count them
+  for (int k = 0; k < kMaxChunks; ++k) pub.need[k] = 0;
+  auto count = [&](int r0, int r1) {
+    for (uint64_t m = chunk_mask(r0, std::min(r1, g.M), pub.S, pub.n); m != 0; m &= m - 1) ++pub.need[__builtin_ctzll(m)];
+  };
+  for (int64_t L = 0; L < T; ++L) {
+    int tm, tn;
+    tile_coords_pub(int(L), sk.tiles_m, sk.tiles_n, pub, &tm, &tn);
+    if (L < whole) {
+      count(tm * 256, tm * 256 + 256);
+    } else {
+      count(tm * 256, tm * 256 + 128);
+      count(tm * 256 + 128, tm * 256 + 256);
+    }
+  }
+  if (whole > 0) {
+    sk.dp_units = int(whole);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 256, true>), dim3(unsigned(whole)), dim3(kGemmThreads), 0, s, g, sk, pub);
+  }
+  if (halves) {
+    GemmSched sh = sk;
+    sh.dp_units = int(2 * tail);
+    sh.unit_base = int(dp);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 128, true>), dim3(unsigned(2 * tail)), dim3(kGemmThreads), 0, s, g, sh,
+                       pub);
+  }
 }
 
 template <int EPI>
@@ -712,6 +778,13 @@ int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle) {
       (void)hipGetLastError();
       return fail(PBLOCK_ERR_NOMEM, std::string("hipMalloc workspace: ") + hipGetErrorString(e));
     }
+    e = hipMemset(static_cast<char*>(h->ws) + h->lay.counters, 0, size_t(kMaxChunks * 4));
+    if (e != hipSuccess) {
+      (void)hipFree(h->ws);
+      delete h;
+      (void)hipGetLastError();
+      return fail(PBLOCK_ERR_HIP, std::string("hipMemset chunk counters: ") + hipGetErrorString(e));
+    }
     *out_handle = h;
     return PBLOCK_OK;
   } catch (...) {
@@ -836,6 +909,98 @@ int pblock_forward_static(const void* x, const pblock_weights* w, const pblock_c
     Timer tm;  // no timing: no handle
     enqueue_forward(ws, x, w, c, dm, out, static_cast<hipStream_t>(stream), &tm);
     return launch_status("pblock_forward_static launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int pblock_forward_rowchunks(pblock_t h, const void* x, const pblock_weights* w, const pblock_cfg* cfg, void* out,
+                             int32_t n_chunks, uint32_t* flags, uint32_t epoch, void* stream) {
+  try {
+    Dims dm;
+    int st = check_forward(h, x, w, cfg, out, &dm);
+    if (st != PBLOCK_OK) return st;
+    const pblock_cfg& c = *cfg;
+    if (c.dtype != PBLOCK_BF16) return fail(PBLOCK_ERR_DTYPE, "the row-chunk publication is bf16 only");
+    if (n_chunks < 1 || n_chunks > std::min(c.S, kMaxChunks))
+      return fail(PBLOCK_ERR_ARG, "n_chunks must be in [1, min(S, 64)]");
+    if (!flags) return fail(PBLOCK_ERR_NULL, "flags is NULL");
+    if ((reinterpret_cast<uintptr_t>(flags) & 3u) != 0) return fail(PBLOCK_ERR_ALIGN, "flags must be 4-byte aligned");
+    if (epoch == 0) return fail(PBLOCK_ERR_ARG, "epoch must be nonzero");
+    const int64_t xb = dm.M * c.d * 2;
+    if (overlap(flags, n_chunks * 4, out, xb) || overlap(flags, n_chunks * 4, x, xb) ||
+        overlap(flags, n_chunks * 4, w->w_in, dm.n_in * c.d * 2) ||
+        overlap(flags, n_chunks * 4, w->w_out, int64_t(c.d) * dm.k_out * 2))
+      return fail(PBLOCK_ERR_ALIAS, "flags overlap out, x or a weight");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Ws ws = workspace(h);
+    Timer tm;
+    st = tm.begin(h, s);
+    if (st != PBLOCK_OK) return st;
+    const int64_t A = dm.A;
+    run_layernorm(x, w->ln_gamma, w->ln_beta, ws.u, dm.M, c, s);
+    tm.mark(0);
+    run_gemm_in(ws.u, c.d, w->w_in, c.d, dm.M, dm.n_in, c.d, ws.qkv, 3 * A, ws.ag, dm.k_out, A, 3 * A, c.dtype, ws.scr,
+                s);
+    tm.mark(1);
+    launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
+    tm.mark(2);
+    GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(ws.ag); g.lda = dm.k_out;
+    g.b = static_cast<const uint16_t*>(w->w_out); g.ldb = dm.k_out;
+    g.M = int(dm.M); g.N = c.d; g.K = int(dm.k_out);
+    g.out0 = static_cast<uint16_t*>(out); g.ld0 = c.d;
+    g.resid = c.add_residual ? static_cast<const uint16_t*>(x) : nullptr; g.ldr = c.d;
+    RowPublish pub{};
+    pub.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(h->ws) + h->lay.counters);
+    pub.flags = flags;
+    pub.epoch = epoch;
+    pub.n = n_chunks;
+    pub.S = c.S;
+    pub.B = c.B;
+    // M-tiles per group of the publication order: about the 256-row tiles of one chunk
+    pub.group_m = int(std::max<int64_t>(1, std::min<int64_t>(kGroupM, (dm.M / n_chunks + 128) / 256)));
+    launch_gemm_bf16_publish<kEpiResidual>(g, ws.scr, pub, s);
+    tm.mark(3);
+    h->last_m = dm.M;
+    return launch_status("pblock_forward_rowchunks launch");
+  } catch (...) {
+    return fail(PBLOCK_ERR_ARG, "internal error");
+  }
+}
+
+int pblock_pack_chunks(const void* out, const pblock_cfg* cfg, int32_t n_chunks, const uint32_t* flags, uint32_t epoch,
+                       void* send, uint64_t* stamps, void* stream) {
+  try {
+    if (!out || !flags || !send || !stamps) return fail(PBLOCK_ERR_NULL, "out, flags, send or stamps is NULL");
+    int st = validate(cfg);
+    if (st != PBLOCK_OK) return st;
+    const pblock_cfg& c = *cfg;
+    if (c.dtype != PBLOCK_BF16) return fail(PBLOCK_ERR_DTYPE, "the row-chunk publication is bf16 only");
+    if (n_chunks < 1 || n_chunks > std::min(c.S, kMaxChunks))
+      return fail(PBLOCK_ERR_ARG, "n_chunks must be in [1, min(S, 64)]");
+    if (!aligned16(out) || !aligned16(send) || (reinterpret_cast<uintptr_t>(flags) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(stamps) & 7u) != 0)
+      return fail(PBLOCK_ERR_ALIGN, "out and send 16-byte, flags 4-byte, stamps 8-byte aligned");
+    const int64_t bytes = int64_t(c.B) * c.S * c.d * 2;
+    if (overlap(send, bytes, out, bytes) || overlap(stamps, n_chunks * 8, out, bytes) ||
+        overlap(stamps, n_chunks * 8, send, bytes) || overlap(flags, n_chunks * 4, send, bytes) ||
+        overlap(stamps, n_chunks * 8, flags, n_chunks * 4))
+      return fail(PBLOCK_ERR_ALIAS, "send, stamps, flags and out must not overlap");
+    st = check_device(nullptr);
+    if (st != PBLOCK_OK) return st;
+    PackArgs a{};
+    a.out = static_cast<const uint16_t*>(out);
+    a.send = static_cast<uint16_t*>(send);
+    a.flags = flags;
+    a.stamps = reinterpret_cast<unsigned long long*>(stamps);
+    a.epoch = epoch;
+    a.B = c.B; a.S = c.S; a.d = c.d; a.n = n_chunks;
+    a.wgs_per_chunk = std::max(1, 32 / n_chunks);  // at most 32 workgroups (n <= 32): one per CU of a small mask
+    a.timeout_ticks = kPackTimeoutTicks;
+    hipLaunchKernelGGL(pack_chunks_kernel, dim3(unsigned(n_chunks * a.wgs_per_chunk)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+    return launch_status("pblock_pack_chunks launch");
   } catch (...) {
     return fail(PBLOCK_ERR_ARG, "internal error");
   }
