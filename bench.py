@@ -7,11 +7,18 @@ one 1/8 tensor-parallel shard of the 175B layer (B=1, S=2048, d=12288, 12
 local heads x 128, local ffn 6144, W=512), emitting the pre-reduce-scatter
 partial.
 
+Order of a run: W warm-up steps, the timed region (exactly K steps between two
+events: `value`, `ms_per_step`), then the same K steps again with HIP events
+around every step and every kernel launch (`instrumented`: the per-step spread,
+the per-kernel times and the roofline record of the dominant kernel), then the
+other measurements.  From a cold start the forward needs about 30 steps to reach
+its sustained rate (`--ramp`), so with few warm-up steps the timed region
+includes part of that ramp.
+
 Prints ONE JSON line: throughput in TFLOP/s of algorithmic work, % of the bf16
-MFMA peak, tokens/s, step-time median / p10 / p90, a cold-cache pass, per-kernel
-times measured with HIP events inside the timed region, the roofline record of
-the dominant kernel, the rate of a register-only MFMA loop measured in the same
-run, and the fp64 CPU oracle timed on the host as a baseline.
+MFMA peak, tokens/s, the instrumented pass, a cold-cache pass, per-kernel times,
+the roofline record, the MFMA-loop rate, and the fp64 CPU oracle timed on the
+host as a baseline.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload shard175b]
                   [--block parallel|serial] [--window W] [--chunks N]
@@ -40,8 +47,9 @@ COLD_SCRUB_MIB = 512       # written between cold-cache steps (more than the 256
 MEASURED_TRAFFIC_BYTES = {
     # gemm_in main kernel + its split-K tail reduce (profiles/shard175b_kernels.md); set
     # only for the GEMM build the counters were taken on (4-wave 128x128, 64-deep slabs, row-major split-K
-    # partials, epilogue with the variant steps and the 5-term erfc GeLU)
-    "shard175b": 1024086000,
+    # partials, epilogue with the variant steps and the 5-term erfc GeLU; tile-height and row-chunk
+    # publication template parameters, off for this launch)
+    "shard175b": 1023796000,
 }
 
 WORKLOAD_NOTES = {
@@ -84,6 +92,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (for HBM counter calibration) and exit")
+    p.add_argument("--ramp", action="store_true",
+                   help="only measure from a cold start: per-step times of the forward over its first 120 steps "
+                        "after 5 warm-up steps, then 60 steps each with the per-kernel timing events on, off, on")
     p.add_argument("--sweep", action="store_true",
                    help="only time the attention kernel over windows and sequence lengths and fit time vs keys")
     return p.parse_args()
@@ -318,6 +329,31 @@ def main():
                  "dln_beta": torch.empty_like(dev["beta"]), "dw_in": torch.empty_like(dev["w_in"]),
                  "dw_out": torch.empty_like(dev["w_out"])}
 
+    if args.ramp:
+        def series(n, timing):
+            tb.pblock_set_timing(h, timing)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            ev[0].record(stream)
+            for i in range(n):
+                tb.pblock_forward(h, dev["x"], weights, cfg, out, stream)
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            tb.pblock_set_timing(h, False)
+            return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+        for _ in range(5):
+            tb.pblock_forward(h, dev["x"], weights, cfg, out, stream)
+        torch.cuda.synchronize()
+        cold_start = series(120, False)
+        on1, off, on2 = series(60, True), series(60, False), series(60, True)
+        print(json.dumps({
+            "ramp": f"{cfg.name} forward from a cold start, 5 warm-up steps, then one event per step",
+            "median_ms_per_10_steps": [round(percentile(cold_start[i:i + 10], 0.5), 5) for i in range(0, 120, 10)],
+            "per_kernel_events_on_off_on_median_ms": [round(percentile(v, 0.5), 5) for v in (on1, off, on2)],
+        }), flush=True)
+        tb.pblock_destroy(h)
+        return
+
     def step(chunked=bool(args.chunks)):
         if args.train:
             tb.pblock_forward_train(h, dev["x"], weights, cfg, out, train_ws, stream)
@@ -339,37 +375,57 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
 
+    # The timed region: exactly K steps between two events, nothing else recorded in it (per-kernel
+    # events would add ~2% to each step).
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    t0.record(stream)
+    for i in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = t0.elapsed_time(t1)
+    print(f"[bench] timed {args.steps} steps in {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms)", file=sys.stderr,
+          flush=True)
+
+    # The same K steps again with HIP events around every step and every kernel launch (the
+    # library's per-kernel timing, on the stream the kernels run on): the per-step spread, the
+    # per-kernel times and the roofline record come from here.
     tb.pblock_set_timing(h, True)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t_wall = time.perf_counter()
     marks[0].record(stream)
     for i in range(args.steps):
         step()
         marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_total = marks[0].elapsed_time(marks[-1])
+    ms_instrumented = marks[0].elapsed_time(marks[-1])
     step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     kernel_ms, n_fwd = tb.pblock_kernel_times(h, backward=args.train)
     if args.train:
         n_fwd //= 2  # a forward and a backward call per step
     tb.pblock_set_timing(h, False)
-    print(f"[bench] timed {args.steps} steps in {ms_total:.3f} ms (wall {wall * 1e3:.3f} ms)", file=sys.stderr,
-          flush=True)
 
     chunking = None
     published_us = None
+    # completion of each chunk's rows of out within the last timed step (before any more steps)
+    t_done = [marks[-2].elapsed_time(e) for e in done] if args.chunks and not args.rowchunks else None
     if args.chunks:
-        # the same forward unchunked, untimed per kernel, for the ratio
-        u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n_un = max(5, args.steps // 3)
-        u0.record(stream)
-        for _ in range(n_un):
-            step(chunked=False)
-        u1.record(stream)
-        torch.cuda.synchronize()
-        unchunked = u0.elapsed_time(u1) / n_un
+        # the chunked and the unchunked forward in alternating rounds of 10 steps (5 rounds each),
+        # for a ratio that clock and temperature drift over the run does not bias
+        ab = {False: [], True: []}
+        for _ in range(5):
+            for chunked_round in (False, True):
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                for _ in range(10):
+                    step(chunked=chunked_round)
+                a1.record(stream)
+                torch.cuda.synchronize()
+                ab[chunked_round].append(a0.elapsed_time(a1) / 10)
+        unchunked, chunked_alt = percentile(ab[False], 0.5), percentile(ab[True], 0.5)
     if args.rowchunks:
         # one more step with the consumer on a second stream: when each chunk's flag was seen
         send = torch.empty_like(out)
@@ -392,8 +448,6 @@ def main():
             published_us = [round((v - min(st)) / 100.0, 2) for v in st]  # 100 MHz device clock
             print(f"[bench] chunk publication (us after the first): {published_us}", file=sys.stderr, flush=True)
     if args.chunks:
-        # completion of each chunk's rows of out within the last timed step
-        t_done = [marks[-2].elapsed_time(e) for e in done] if not args.rowchunks else None
         # the same forward unchunked, with per-kernel timing, for the kernel and roofline figures
         tb.pblock_set_timing(h, True)
         for _ in range(max(5, args.steps // 3)):
@@ -406,7 +460,8 @@ def main():
                     "chunk_done_ms": [round(v, 5) for v in t_done] if t_done else None,
                     "published_us_after_first": published_us,
                     "unchunked_ms_per_step": round(unchunked, 5),
-                    "chunked_over_unchunked": round((ms_total / args.steps) / unchunked, 4)}
+                    "alternating_rounds_ms": {"chunked": round(chunked_alt, 5), "unchunked": round(unchunked, 5)},
+                    "chunked_over_unchunked": round(chunked_alt / unchunked, 4)}
         if t_done:
             print(f"[bench] chunk completion (ms into the step): {[round(v, 3) for v in t_done]}", file=sys.stderr,
                   flush=True)
@@ -496,8 +551,11 @@ def main():
         "pct_peak_bf16": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.M / (ms_step * 1e-3), 1),
         "algorithmic_gflop_per_step": round(flops / 1e9, 3),
-        "step_ms": {"median": round(percentile(step_ms, 0.5), 5), "p10": round(percentile(step_ms, 0.1), 5),
-                    "p90": round(percentile(step_ms, 0.9), 5)},
+        # the instrumented pass of the same K steps (events around every step and kernel launch)
+        "instrumented": {"ms_per_step": round(ms_instrumented / args.steps, 5),
+                         "step_ms": {"median": round(percentile(step_ms, 0.5), 5),
+                                     "p10": round(percentile(step_ms, 0.1), 5),
+                                     "p90": round(percentile(step_ms, 0.9), 5)}},
         "cold_cache": cold,
         "chunking": chunking,
         "mfma_loop_tflops": round(mfma_tflops, 1),
