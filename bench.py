@@ -95,6 +95,9 @@ def parse():
     p.add_argument("--ramp", action="store_true",
                    help="only measure from a cold start: per-step times of the forward over its first 120 steps "
                         "after 5 warm-up steps, then 60 steps each with the per-kernel timing events on, off, on")
+    p.add_argument("--vs-torch-gemm", action="store_true",
+                   help="only compare each workload's two GEMMs (the library's, epilogues included) with "
+                        "torch.nn.functional.linear (hipBLASLt) on the same bf16 operands")
     p.add_argument("--sweep", action="store_true",
                    help="only time the attention kernel over windows and sequence lengths and fit time vs keys")
     return p.parse_args()
@@ -185,6 +188,68 @@ def mfma_loop_rate(tb, torch, stream) -> float:
     return wgs * 4 * iters * 16 * 32768 / (s.elapsed_time(e) * 1e-3) / 1e12
 
 
+def gemm_vs_torch() -> None:
+    """Per bf16 workload: the library's input GEMM (with its GeLU epilogue and split-K tail) and
+    output GEMM (with its tail launch) from its per-kernel events over 30 forwards, against
+    torch.nn.functional.linear (hipBLASLt) on the same operand shapes and data, 30 calls each
+    after 5 untimed ones; algorithmic TFLOP/s of each."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    import transformer_block_fwd_amd as tb
+    from workload import CONFIGS, make_inputs
+
+    rows = []
+    for name in ("small", "shard175b", "long", "fullcausal"):
+        cfg = CONFIGS[name]
+        inp = make_inputs(cfg, seed=0)
+        dev = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).cuda()
+               for k, v in inp.device_arrays().items()}
+        w = (dev["gamma"], dev["beta"], dev["w_in"], dev["w_out"])
+        out = torch.empty_like(dev["x"])
+        h = tb.pblock_create(cfg)
+        for _ in range(5):
+            tb.pblock_forward(h, dev["x"], w, cfg, out)
+        tb.pblock_set_timing(h, True)
+        for _ in range(30):
+            tb.pblock_forward(h, dev["x"], w, cfg, out)
+        ms, n = tb.pblock_kernel_times(h)
+        tb.pblock_set_timing(h, False)
+        tb.pblock_destroy(h)
+        M = cfg.M
+        x2 = dev["x"].view(M, cfg.d)
+        ag = torch.randn(M, cfg.k_out, device="cuda").to(torch.bfloat16)
+
+        def t_linear(a, b, reps=30):
+            for _ in range(5):
+                F.linear(a, b)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                F.linear(a, b)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        t_in, t_out = t_linear(x2, dev["w_in"]), t_linear(ag, dev["w_out"])
+        for gemm, ours, theirs, fl, shape in (
+                ("in", ms["gemm_in"] / n, t_in, cfg.gemm1_flops(), (M, cfg.n_in, cfg.d)),
+                ("out", ms["gemm_out"] / n, t_out, cfg.gemm2_flops(), (M, cfg.d, cfg.k_out))):
+            rows.append({"workload": name, "gemm": gemm, "MxNxK": "x".join(map(str, shape)),
+                         "library_ms": round(ours, 5), "library_tflops": round(fl / (ours * 1e-3) / 1e12, 1),
+                         "torch_linear_ms": round(theirs, 5), "torch_linear_tflops": round(fl / (theirs * 1e-3) / 1e12, 1),
+                         "library_over_torch_time": round(ours / theirs, 3)})
+            print(f"[gemm] {name} {gemm} {rows[-1]['MxNxK']}: library {ours * 1e3:.1f} us, torch linear "
+                  f"{theirs * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del dev, out, ag
+        torch.cuda.empty_cache()
+    print(json.dumps({"gemm_vs_torch_linear": rows,
+                      "note": "library GEMMs include their epilogues (GeLU on FC1 columns; residual store) and tail "
+                              "launches; torch linear is a plain bf16 GEMM"}), flush=True)
+
+
 def attention_sweep() -> None:
     """Attention kernel time against the number of (query, key) pairs it must score:
     W in {128 .. 2048} at S = 8192 and S in {2048, 4096} at W = 1024 (the long
@@ -262,6 +327,9 @@ def main():
         return
     if args.sweep:
         attention_sweep()
+        return
+    if args.vs_torch_gemm:
+        gemm_vs_torch()
         return
 
     cfg = CONFIGS[args.workload]
