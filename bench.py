@@ -173,16 +173,17 @@ def percentile(v, q):
     return s[lo] + (s[hi] - s[lo]) * (k - lo)
 
 
-def mfma_loop_rate(tb, torch, stream) -> float:
-    """TFLOP/s of the library's register-only MFMA loop over all CUs (about 20 ms)."""
+def mfma_loop_rate(tb, torch, stream, form: str = "16x16x32") -> float:
+    """TFLOP/s of the library's register-only MFMA loop over all CUs (about 20 ms), of the GEMMs'
+    16x16x32 instruction or of the 32x32x16 one."""
     wgs = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
     iters = 4000
-    tb.pblock_mfma_loop(wgs, 100, sink, stream)
+    tb.pblock_mfma_loop(wgs, 100, sink, stream, form=form)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record(stream)
-    tb.pblock_mfma_loop(wgs, iters, sink, stream)
+    tb.pblock_mfma_loop(wgs, iters, sink, stream, form=form)
     e.record(stream)
     torch.cuda.synchronize()
     return wgs * 4 * iters * 16 * 32768 / (s.elapsed_time(e) * 1e-3) / 1e12
@@ -566,7 +567,9 @@ def main():
     copy_gbs = 2 * dev["x"].numel() * dev["x"].element_size() / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9
 
     mfma_tflops = mfma_loop_rate(tb, torch, stream)
-    print(f"[bench] register-only MFMA loop {mfma_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    mfma32_tflops = mfma_loop_rate(tb, torch, stream, form="32x32x16")
+    print(f"[bench] register-only MFMA loop {mfma_tflops:.1f} TFLOP/s (16x16x32; 32x32x16: {mfma32_tflops:.1f})",
+          file=sys.stderr, flush=True)
 
     ms_step = ms_total / args.steps
     flops = cfg.flops() + (backward_flops(cfg) if args.train else 0.0)
@@ -627,6 +630,7 @@ def main():
         "cold_cache": cold,
         "chunking": chunking,
         "mfma_loop_tflops": round(mfma_tflops, 1),
+        "mfma_loop_32x32x16_tflops": round(mfma32_tflops, 1),
         "pct_of_mfma_loop": round(100 * tflops / mfma_tflops, 2),
         "kernels": per_kernel,
         "roofline": roofline,

@@ -385,15 +385,22 @@ enum {
 };
 int pblock_activation(const float* z, float* out, int64_t n, int32_t form, void* stream);
 
-/* Measurement aid, not part of the block: a register-only loop of
- * v_mfma_f32_32x32x16_bf16 (the GEMMs' instruction) on `workgroups` workgroups
- * of 4 wavefronts, each wavefront issuing 16 independent MFMAs per iteration,
- * `iterations` times; it performs workgroups * 4 * iterations * 16 * 32768
- * FLOP and writes one float per thread to sink (workgroups * 256 floats, caller
- * owned, device memory).  Timing it gives the MFMA rate the chip sustains at
- * its present clock and power state, the ceiling the GEMMs are compared with.
- * workgroups >= 1, iterations >= 1.  Enqueued on `stream`, no sync. */
-int pblock_mfma_loop(int32_t workgroups, int32_t iterations, float* sink, void* stream);
+/* Measurement aid, not part of the block: a register-only loop of bf16 MFMAs on
+ * `workgroups` workgroups of 4 wavefronts, each wavefront issuing independent
+ * MFMAs worth 16 * 32768 FLOP per iteration, `iterations` times; it performs
+ * workgroups * 4 * iterations * 16 * 32768 FLOP and writes one float per thread
+ * to sink (workgroups * 256 floats, caller owned, device memory).  form picks
+ * the instruction: PBLOCK_MFMA_16X16X32 (v_mfma_f32_16x16x32_bf16, the GEMMs'
+ * instruction; 32 per iteration) or PBLOCK_MFMA_32X32X16
+ * (v_mfma_f32_32x32x16_bf16; 16 per iteration).  Timing it gives the MFMA rate
+ * the chip sustains at its present clock and power state, the ceiling the GEMMs
+ * are compared with.  workgroups >= 1, iterations >= 1, an unknown form is
+ * PBLOCK_ERR_ARG.  Enqueued on `stream`, no sync. */
+enum {
+  PBLOCK_MFMA_16X16X32 = 0,
+  PBLOCK_MFMA_32X32X16 = 1
+};
+int pblock_mfma_loop(int32_t workgroups, int32_t iterations, int32_t form, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

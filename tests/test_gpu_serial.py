@@ -161,12 +161,15 @@ def test_serial_timing_categories():
 
 
 def test_mfma_loop_runs():
-    """The measurement aid's register-only MFMA loop completes and writes finite sums."""
+    """The measurement aid's register-only MFMA loops (both forms, even and odd iteration counts) complete
+    and write finite sums."""
     import torch
 
     import transformer_block_fwd_amd as tb
 
-    sink = torch.full((8 * 256,), float("nan"), dtype=torch.float32, device="cuda")
-    tb.pblock_mfma_loop(8, 10, sink)
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(sink).all())
+    for form in ("16x16x32", "32x32x16"):
+        for iters in (10, 11):
+            sink = torch.full((8 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+            tb.pblock_mfma_loop(8, iters, sink, form=form)
+            torch.cuda.synchronize()
+            assert bool(torch.isfinite(sink).all()), (form, iters)

@@ -34,7 +34,7 @@ __all__ = [
     "PblockGrads", "pblock_train_workspace_bytes", "pblock_forward_train", "pblock_backward",
     "pblock_forward_serial", "pblock_forward_chunked", "pblock_mfma_loop", "as_cfg", "BACKWARD_KERNEL_NAMES",
     "pblock_activation", "ACTIVATION_FORMS", "pblock_forward_static", "pblock_forward_rowchunks",
-    "pblock_pack_chunks",
+    "pblock_pack_chunks", "MFMA_FORMS",
 ]
 
 KERNEL_NAMES = ("layernorm", "gemm_in", "attention", "gemm_out")
@@ -311,12 +311,19 @@ def _check_words(t, name, itemsize, n):
         raise ValueError(f"{name} must be a contiguous GPU tensor of {itemsize}-byte words with >= {n} elements")
 
 
-def pblock_mfma_loop(workgroups: int, iterations: int, sink, stream=None) -> None:
-    """Measurement aid: register-only MFMA loop, workgroups * 4 * iterations * 16 * 32768 FLOP; sink is a
-    float32 GPU tensor of at least workgroups * 256 elements."""
+MFMA_FORMS = {"16x16x32": _abi.PBLOCK_MFMA_16X16X32, "32x32x16": _abi.PBLOCK_MFMA_32X32X16}
+
+
+def pblock_mfma_loop(workgroups: int, iterations: int, sink, stream=None, form: str = "16x16x32") -> None:
+    """Measurement aid: register-only bf16 MFMA loop, workgroups * 4 * iterations * 16 * 32768 FLOP, of
+    the GEMMs' 16x16x32 instruction or of the 32x32x16 one (form); sink is a float32 GPU tensor of at
+    least workgroups * 256 elements."""
     if sink.dtype.itemsize != 4 or sink.numel() < workgroups * 256 or not sink.is_cuda:
         raise ValueError("sink must be a float32 GPU tensor of at least workgroups * 256 elements")
-    _abi.check(_abi.lib().pblock_mfma_loop(int(workgroups), int(iterations), _ptr(sink), _stream(stream)),
+    if form not in MFMA_FORMS:
+        raise ValueError(f"form must be one of {sorted(MFMA_FORMS)}")
+    _abi.check(_abi.lib().pblock_mfma_loop(int(workgroups), int(iterations), MFMA_FORMS[form], _ptr(sink),
+                                           _stream(stream)),
                "pblock_mfma_loop")
 
 

@@ -33,6 +33,8 @@ PBLOCK_ACT_GELU_ERF_F32 = 0
 PBLOCK_ACT_GELU_ERF_BF16 = 1
 PBLOCK_ACT_GELU_TANH = 2
 PBLOCK_ACT_GELU_ERF_GRAD = 3
+PBLOCK_MFMA_16X16X32 = 0
+PBLOCK_MFMA_32X32X16 = 1
 
 
 class PblockCfg(ctypes.Structure):
@@ -114,7 +116,7 @@ _SIGNATURES = {
                                         _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_void_p]),
     "pblock_forward_serial": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights), _c.c_void_p,
                                          _c.c_void_p, _c.POINTER(PblockCfg), _c.c_void_p, _c.c_void_p]),
-    "pblock_mfma_loop": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
+    "pblock_mfma_loop": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
     "pblock_forward_variant": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.POINTER(PblockWeights),
                                           _c.POINTER(PblockVariantWeights), _c.POINTER(PblockCfg),
                                           _c.POINTER(PblockVariant), _c.c_void_p, _c.c_void_p]),

@@ -1,12 +1,14 @@
 // bf16 GEMM on gfx950 matrix cores: C[m, n] = sum_k X[m, k] * Wt[n, k].
 //
 // Both operands are K-contiguous (activations [M, K] and nn.Linear-style
-// weights [N, K]), which is what the 32x32x16 bf16 MFMA wants: every lane
+// weights [N, K]), which is what the 16x16x32 bf16 MFMA wants: every lane
 // feeds 8 consecutive k of one row from a single 16-byte LDS read.
 //
 // Tile: 256 x 256 outputs per workgroup of 4 wavefronts (one per SIMD), laid
-// out 2 (M) x 2 (N); each wavefront owns 128 x 128 as 4 x 4 MFMA tiles of
-// 32 x 32 whose fp32 accumulators (256 per lane) live in the AGPR file.
+// out 2 (M) x 2 (N); each wavefront owns 128 x 128 as 8 x 8 MFMA tiles of
+// 16 x 16 whose fp32 accumulators (256 per lane) live in the AGPR file.  The
+// 16x16x32 form sustains more throughput on this chip than 32x32x16 at the same
+// operand traffic (it moves fewer accumulator bits per flop).
 //
 // Pipeline: the k loop walks 64-wide slabs through two LDS stages (each an A
 // and a B array of 32 KiB, separately named so the compiler can see that
@@ -14,16 +16,15 @@
 // into LDS with global_load_lds_dwordx4; one instruction fills 1 KiB = 8 rows
 // of 128 bytes, the 16-byte chunk index inside a row XORed with
 // ((row >> 1) & 7) on the source side and undone on the fragment reads (the 16
-// rows one read pass touches then hit 16 distinct bank groups).  Within a
-// slab (four 16-deep k-steps of 16 MFMAs per wavefront):
-//   k-step 0: its MFMAs run while the fragments of k-steps 1..3 are read, so
-//     the whole stage is consumed early; a barrier then frees it;
-//   k-steps 1..3: the copies of slab t+2 into the freed stage are spread over
-//     these MFMAs (6 + 4 + 6 instructions per wavefront), so the load unit sees
-//     an even stream instead of a burst;
-//   before k-step 3: wait for this wave's copies of slab t+1, barrier, and
-//     read k-step 0 of slab t+1 behind the k-step 3 MFMAs.
-// The MFMA / LDS-read / copy interleave is pinned with sched_group_barrier.
+// rows one read pass touches then hit 16 distinct bank groups).  A slab is two
+// 32-deep k-steps of 64 MFMAs per wavefront, run as four phases of 32:
+//   phase 1 (k-step 0, rows 0..3): the fragments of k-step 1 are read behind
+//     its MFMAs, so the whole stage is consumed early; a barrier then frees it;
+//   phases 2, 3: the copies of slab t+2 into the freed stage are spread over
+//     the MFMAs (6 + 4 instructions per wavefront);
+//   before phase 4: wait for this wave's copies of slab t+1, barrier; phase 4
+//     issues the last 6 copies and reads k-step 0 of slab t+1 behind its MFMAs.
+// The interleave is written out in program order (see the phase lambda).
 //
 // Operand bounds: A rows are read up to the end of the last 256-row tile (the
 // caller allocates A in whole 256-row tiles; rows past M are never stored); B
@@ -270,7 +271,9 @@ template <int EPI, int BM = kGemmBM, bool PUB = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, GemmSched sk, RowPublish pub) {
   static_assert(BM == 256 || BM == 128, "tile height 256 or 128");
   constexpr int BN = kGemmBN, BK = kGemmBK, NT = kGemmThreads;
-  constexpr int FM = BM / 64, FN = 4;  // 32x32 MFMA tiles per wavefront (BM/2 x 128)
+  constexpr int MI = BM / 32, NJ = 8;  // 16x16 MFMA tiles per wavefront (BM/2 x 128)
+  constexpr int P = MI * NJ / 2;       // MFMAs per phase (half a 32-deep k-step)
+  constexpr int NR = MI + NJ;          // fragment reads per k-step
   constexpr int NA = BM / 32;          // A copy instructions per wavefront and slab (B: 8)
   // copy instructions of slab t+2 issued in k-steps 1, 2 and 3 (A then B counts)
   constexpr int CA1 = NA < 3 ? NA : 3, CA2 = (NA < 5 ? NA : 5) - CA1, CA3 = NA - CA1 - CA2;
@@ -284,7 +287,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lg = lane >> 5;
 
   int L, kb, ke, tl = -1, chunk = 0;
   if (PUB) {
@@ -333,112 +335,114 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   // A: wave w's NA instructions fill rows w*BM/4 .. +BM/4 (1 KiB block w*NA + i = rows
   // w*BM/4 + 8i + l/8: the same row swizzle, since BM/4 is a multiple of 16)
   const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(g.a) + int64_t(m0 + wave * (BM / 4)) * lda_b;
-  // copy instructions i0 .. i1-1 (an A instruction for i < NA, a B instruction each) of slab kt
-  auto issue = [&](int kt, uint16_t* sa, uint16_t* sb, int i0, int i1) __attribute__((always_inline)) {
+  // copy instruction i of slab kt: A (i < NA) and B (i < 8)
+  auto issue_a = [&](int kt, uint16_t* sa, int i) __attribute__((always_inline)) {
     const uint32_t kofs = uint32_t(kt) * (BK * 2);
+    __builtin_amdgcn_global_load_lds(a_blk + int64_t(8 * i) * lda_b + kofs + offa[i & 1],
+                                     (PBLK_LDS void*)(sa + (wave * NA + i) * 512), 16, 0, 0);
+  };
+  auto issue_b = [&](int kt, uint16_t* sb, int i) __attribute__((always_inline)) {
+    const uint32_t kofs = uint32_t(kt) * (BK * 2);
+    const int brow = min(n0 + wave * 64 + 8 * i, g.N - 8);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(g.b) + int64_t(brow) * ldb_b + kofs + offb[i & 1],
+                                     (PBLK_LDS void*)(sb + (wave * 8 + i) * 512), 16, 0, 0);
+  };
+  // copy instructions i0 .. i1-1 of slab kt
+  auto issue = [&](int kt, uint16_t* sa, uint16_t* sb, int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      if (i < NA)
-        __builtin_amdgcn_global_load_lds(a_blk + int64_t(8 * i) * lda_b + kofs + offa[i & 1],
-                                         (PBLK_LDS void*)(sa + (wave * NA + i) * 512), 16, 0, 0);
-      const int brow = min(n0 + wave * 64 + 8 * i, g.N - 8);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(g.b) + int64_t(brow) * ldb_b + kofs + offb[i & 1],
-                                       (PBLK_LDS void*)(sb + (wave * 8 + i) * 512), 16, 0, 0);
+      if (i < NA) issue_a(kt, sa, i);
+      issue_b(kt, sb, i);
     }
   };
 
-  // Fragment reads: row w*128 + i*32 + lr, logical chunk 2kk + lg at physical chunk
-  // (2kk + lg) ^ ((lr >> 1) & 7); byte offsets within an operand tile.
-  uint32_t rda[4], rdb[4];
+  // Fragment reads (16x16x32 operands): lane l reads row 16 * block + l % 16, the 8 k of
+  // logical chunk 4 ks + l / 16 of k-step ks, at physical chunk (4 ks + l / 16) ^ ((l % 16 >> 1) & 7);
+  // byte offsets within an operand tile.
+  const int lr = lane & 15, lq = lane >> 4;
+  uint32_t rda[2], rdb[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const uint32_t o = uint32_t(lr * 128 + (((2 * kk + lg) ^ ((lr >> 1) & 7)) << 4));
-    rda[kk] = o + uint32_t(wm * (BM / 2) * 128);
-    rdb[kk] = o + uint32_t(wn * 128 * 128);
+  for (int ks = 0; ks < 2; ++ks) {
+    const uint32_t o = uint32_t(lr * 128 + (((4 * ks + lq) ^ ((lr >> 1) & 7)) << 4));
+    rda[ks] = o + uint32_t(wm * (BM / 2) * 128);
+    rdb[ks] = o + uint32_t(wn * 128 * 128);
   }
 
-  f32x16 acc[FM][FN];
+  f32x4 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 fa[4][FM], fb[4][FN];  // one fragment buffer per k-step of a slab
-  auto rd = [&](int buf, const uint16_t* sa, const uint16_t* sb, int kk) __attribute__((always_inline)) {
+  bf16x8 fa[2][MI], fb[2][NJ];  // one fragment buffer per k-step of a slab
+  // Fragment read x (0 .. NR-1) of k-step ks into buffer buf, in the order the MFMAs consume
+  // them: A row block 0, B column blocks 0 .. NJ-1, A row blocks 1 .. MI-1.
+  auto rd1 = [&](int buf, const uint16_t* sa, const uint16_t* sb, int ks, int x) __attribute__((always_inline)) {
     const uint8_t* pa = reinterpret_cast<const uint8_t*>(sa);
     const uint8_t* pb = reinterpret_cast<const uint8_t*>(sb);
-    // in the order the MFMAs consume them
-    fa[buf][0] = *reinterpret_cast<const bf16x8*>(pa + rda[kk]);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8*>(pb + rdb[kk] + j * 32 * 128);
-#pragma unroll
-    for (int i = 1; i < FM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8*>(pa + rda[kk] + i * 32 * 128);
+    if (x == 0) fa[buf][0] = *reinterpret_cast<const bf16x8*>(pa + rda[ks]);
+    else if (x <= NJ) fb[buf][x - 1] = *reinterpret_cast<const bf16x8*>(pb + rdb[ks] + (x - 1) * 16 * 128);
+    else fa[buf][x - NJ] = *reinterpret_cast<const bf16x8*>(pa + rda[ks] + (x - NJ) * 16 * 128);
   };
-  auto mm = [&](int buf) __attribute__((always_inline)) {
+  // One phase: the P MFMAs of k-step buf over fragment rows [h MI/2, (h+1) MI/2) (all NJ column
+  // blocks), with fragment read x (x < nr: k-step rks of stage (rsa, rsb) into buffer rbuf)
+  // and copy slot x (copies i0 .. i1-1 of slab tc into stage (wa, wb): even slots the A
+  // instruction of i0 + x/2 when it exists, odd slots its B instruction) behind MFMA x.
+  //
+  // The MFMA is written as inline asm with its accumulator tied ("+a"): the builtin's untied
+  // 16x16 form lets the register allocator rotate the accumulators through copies on every
+  // loop trip.  Volatile asm also keeps every memory operation in program order around it,
+  // which fixes the interleave written here.  The only hazards left to the code are those of
+  // the accumulators (the fragment registers a read overwrites were last read at least 8
+  // MFMAs earlier): the zeroing before the first MFMA and the epilogue's reads after the last
+  // one are separated from them by explicit wait states.
+  auto phase = [&](int buf, int h, int nr, int rbuf, const uint16_t* rsa, const uint16_t* rsb, int rks, int tc,
+                   uint16_t* wa, uint16_t* wb, int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-  };
-  // sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read
-  // 16 MFMAs with 24 fragment reads behind the first 12
-  auto interleave_rd24 = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int x = 0; x < 12; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  };
-  // 16 MFMAs with n copy instructions and nr fragment reads spread over them
-  auto interleave_cp = [&](int n, int nr) __attribute__((always_inline)) {
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (x < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (x < n) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    for (int x = 0; x < P; ++x) {
+      const int i = h * (MI / 2) + x / NJ, j = x % NJ;
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fb[buf][j]), "v"(fa[buf][i]));
+      if (x < nr) rd1(rbuf, rsa, rsb, rks, x);
+      const int ci = i0 + x / 2;
+      if (ci < i1) {
+        if (x & 1) issue_b(tc, wb, ci);
+        else if (ci < NA) issue_a(tc, wa, ci);
+      }
     }
   };
 
   // Slab t in stage (ca, cb), its k-step 0 fragments requested into buffer 0, the copies of
-  // slab t+1 into stage (na, nb) in flight.
+  // slab t+1 into stage (na, nb) in flight.  Four phases of P MFMAs: k-step 0 then k-step 1,
+  // each in two halves of its fragment rows.
+  //   1: k-step 1's fragments are read behind the first NR MFMAs; then the stage is consumed
+  //      (own reads waited for, a barrier for everyone's) and is free for slab t+2;
+  //   2, 3: the copies of slab t+2 (instructions 0..2, then 3..4), spread over the MFMAs;
+  //   before 4: this wave's copies of slab t+1 landed, a barrier: slab t+1 is complete;
+  //   4: copies 5..7 and the reads of slab t+1's k-step 0 fragments behind the MFMAs.
   auto slab = [&](int t, const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb) __attribute__((always_inline)) {
     uint16_t* wa = const_cast<uint16_t*>(ca);
     uint16_t* wb = const_cast<uint16_t*>(cb);
     const int tc = min(t + 2, ke - 1);  // branch-free: past the end the last slab is fetched again
-    rd(1, ca, cb, 1);
-    rd(2, ca, cb, 2);
-    rd(3, ca, cb, 3);
-    mm(0);
-    interleave_rd24();
-    __builtin_amdgcn_sched_barrier(0);
+    phase(0, 0, NR, 1, ca, cb, 1, tc, wa, wb, 0, 0);
     wait_lgkm0();   // own reads of this stage done
     lds_barrier();  // everyone's: the stage is free
-    issue(tc, wa, wb, 0, 3);
-    mm(1);
-    interleave_cp(C1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(tc, wa, wb, 3, 5);
-    mm(2);
-    interleave_cp(C2, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    phase(0, 1, 0, 0, ca, cb, 0, tc, wa, wb, 0, 3);
+    phase(1, 0, 0, 0, ca, cb, 0, tc, wa, wb, 3, 5);
     wait_vm_lgkm0<C1 + C2>();  // own copies of slab t+1 landed (those of slab t+2 may be in flight)
     lds_barrier();             // everyone's: slab t+1 is complete
-    issue(tc, wa, wb, 5, 8);
-    rd(0, na, nb, 0);
-    mm(3);
-    interleave_cp(C3, 8);
-    __builtin_amdgcn_sched_barrier(0);
+    phase(1, 1, NR, 0, na, nb, 0, tc, wa, wb, 5, 8);
   };
 
   issue(kb, a0, b0, 0, 8);
   issue(min(kb + 1, ke - 1), a1, b1, 0, 8);
   wait_vm_lgkm0<NA + 8>();  // slab kb landed
   lds_barrier();
-  rd(0, a0, b0, 0);
+#pragma unroll
+  for (int x = 0; x < NR; ++x) rd1(0, a0, b0, 0, x);
+  // the accumulators' zeroing (VALU writes) before their first MFMA read
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 4");
+  __builtin_amdgcn_sched_barrier(0);
   const int n = ke - kb;
   int kt = kb;
   for (int p = 0; p + 2 <= n; p += 2, kt += 2) {
@@ -446,25 +450,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     slab(kt + 1, a1, b1, a0, b0);
   }
   if (n & 1) slab(kt, a0, b0, a1, b1);
+  // the last MFMAs' accumulator writes before any other instruction reads them
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no copy may still be writing this workgroup's LDS
 
-  // Epilogue through LDS, FM rounds: in round i every wave stages its rows wm*BM/2 + i*32 +
+  // Epilogue through LDS, BM/64 rounds: in round i every wave stages its rows wm*BM/2 + i*32 +
   // 0..31 as fp32 (stage pair i&1, the wm half in its own array, 16-byte chunks XOR-permuted
   // by row), then all threads store 64 full rows: bf16 outputs with 16-byte writes, or, for a
-  // split-K chunk, its fp32 partial tile (row-major 256 x 256) with 32-byte writes.  Lane
-  // (lr, lg) of MFMA tile (i, j) holds row lr and columns j*32 + 8*(r/4) + 4*lg + r%4.
+  // split-K chunk, its fp32 partial tile (row-major 256 x 256) with 32-byte writes.  Lane l of
+  // MFMA tile (i, j) holds row 16 i + l % 16 and columns 16 j + 4 (l / 16) + 0..3.
   float* part = tl >= 0 ? sk.partials + int64_t(tl * sk.split + chunk) * (BM * BN) : nullptr;
   lds_barrier();  // every wave is past its last fragment read
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < BM / 64; ++i) {
     float* mine = reinterpret_cast<float*>((i & 1) ? (wm ? b1 : a1) : (wm ? b0 : a0));
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int c = wn * 32 + j * 8 + r4 * 2 + lg;
-        const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
-        *reinterpret_cast<f32x4*>(mine + lr * 256 + ((c ^ (lr & 15)) << 2)) = v;
+      for (int j = 0; j < NJ; ++j) {
+        const int row = 16 * h + lr, c = wn * 32 + 4 * j + lq;  // c: 16-byte chunk of the 256 columns
+        *reinterpret_cast<f32x4*>(mine + row * 256 + ((c ^ lr) << 2)) = acc[2 * i + h][j];
       }
     lds_barrier();
 #pragma unroll

@@ -142,17 +142,16 @@ int launch_status(const char* what) {
   return PBLOCK_OK;
 }
 
-// Register-only MFMA loop (measurement aid): operands drawn from the thread id by an
+// Register-only MFMA loops (measurement aid): operands drawn from the thread id by an
 // integer hash so the datapath sees non-trivial bf16 values.
-__global__ __launch_bounds__(256, 1) void mfma_loop_kernel(int iters, float* sink) {
-  const uint32_t s = blockIdx.x * 256u + threadIdx.x;
-  bf16x8 a[4], b[4];
+template <int NOPS>
+__device__ __forceinline__ void hashed_operands(uint32_t s, bf16x8 (&a)[NOPS], bf16x8 (&b)[NOPS]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NOPS; ++i) {
     u32x4 ua, ub;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      uint32_t h = (s * 8u + uint32_t(i) * 4u + uint32_t(e)) * 2654435761u;
+      uint32_t h = (s * 16u + uint32_t(i) * 4u + uint32_t(e)) * 2654435761u;
       h ^= h >> 15;
       h *= 0x2c1b3c6du;
       h ^= h >> 12;
@@ -162,6 +161,13 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(int iters, float* sin
     a[i] = __builtin_bit_cast(bf16x8, ua);
     b[i] = __builtin_bit_cast(bf16x8, ub);
   }
+}
+
+// 32x32x16 form: 16 independent accumulators of 16, 16 MFMAs per iteration.
+__global__ __launch_bounds__(256, 1) void mfma_loop32_kernel(int iters, float* sink) {
+  const uint32_t s = blockIdx.x * 256u + threadIdx.x;
+  bf16x8 a[4], b[4];
+  hashed_operands<4>(s, a, b);
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -182,6 +188,43 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(int iters, float* sin
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) t += acc[i][j][r];
+  sink[s] = t;
+}
+
+// 16x16x32 form (the GEMMs' instruction): 64 accumulators of 4, 32 MFMAs per iteration (the
+// same flops as the 32x32x16 form's 16), run as all 64 every two iterations.  The MFMA is the
+// GEMM's tied inline-asm form, with the same explicit wait states around the loop.
+__global__ __launch_bounds__(256, 1) void mfma_loop16_kernel(int iters, float* sink) {
+  const uint32_t s = blockIdx.x * 256u + threadIdx.x;
+  bf16x8 a[8], b[8];
+  hashed_operands<8>(s, a, b);
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 4");
+  __builtin_amdgcn_sched_barrier(0);
+  auto rows = [&](int i0, int i1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(b[j]), "v"(a[i]));
+  };
+  for (int it = 0; it + 2 <= iters; it += 2) rows(0, 8);
+  if (iters & 1) rows(0, 4);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t += acc[i][j][r];
   sink[s] = t;
 }
 
@@ -1462,14 +1505,15 @@ int pblock_activation(const float* z, float* out, int64_t n, int32_t form, void*
   }
 }
 
-int pblock_mfma_loop(int32_t workgroups, int32_t iterations, float* sink, void* stream) {
+int pblock_mfma_loop(int32_t workgroups, int32_t iterations, int32_t form, float* sink, void* stream) {
   try {
     if (!sink) return fail(PBLOCK_ERR_NULL, "sink is NULL");
     if (workgroups < 1 || iterations < 1) return fail(PBLOCK_ERR_ARG, "workgroups and iterations must be >= 1");
+    if (form != PBLOCK_MFMA_16X16X32 && form != PBLOCK_MFMA_32X32X16) return fail(PBLOCK_ERR_ARG, "unknown MFMA form");
     int st = check_device(nullptr);
     if (st != PBLOCK_OK) return st;
-    hipLaunchKernelGGL(mfma_loop_kernel, dim3(unsigned(workgroups)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       int(iterations), sink);
+    hipLaunchKernelGGL(form == PBLOCK_MFMA_16X16X32 ? mfma_loop16_kernel : mfma_loop32_kernel, dim3(unsigned(workgroups)),
+                       dim3(256), 0, static_cast<hipStream_t>(stream), int(iterations), sink);
     return launch_status("pblock_mfma_loop launch");
   } catch (...) {
     return fail(PBLOCK_ERR_ARG, "internal error");
