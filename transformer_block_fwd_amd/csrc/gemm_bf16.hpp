@@ -20,10 +20,11 @@
 // 32-deep k-steps of 64 MFMAs per wavefront, run as four phases of 32:
 //   phase 1 (k-step 0, rows 0..3): the fragments of k-step 1 are read behind
 //     its MFMAs, so the whole stage is consumed early; a barrier then frees it;
-//   phases 2, 3: the copies of slab t+2 into the freed stage are spread over
-//     the MFMAs (6 + 4 instructions per wavefront);
+//   phases 2..4: the 16 copies of slab t+2 into the freed stage, spread evenly
+//     over their 96 MFMAs (a CU's load path takes about 64 bytes per clock: bursts
+//     of copies stall the MFMAs queued behind them);
 //   before phase 4: wait for this wave's copies of slab t+1, barrier; phase 4
-//     issues the last 6 copies and reads k-step 0 of slab t+1 behind its MFMAs.
+//     also reads k-step 0 of slab t+1 behind its MFMAs.
 // The interleave is written out in program order (see the phase lambda).
 //
 // Operand bounds: A rows are read up to the end of the last 256-row tile (the
@@ -275,9 +276,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   constexpr int P = MI * NJ / 2;       // MFMAs per phase (half a 32-deep k-step)
   constexpr int NR = MI + NJ;          // fragment reads per k-step
   constexpr int NA = BM / 32;          // A copy instructions per wavefront and slab (B: 8)
-  // copy instructions of slab t+2 issued in k-steps 1, 2 and 3 (A then B counts)
-  constexpr int CA1 = NA < 3 ? NA : 3, CA2 = (NA < 5 ? NA : 5) - CA1, CA3 = NA - CA1 - CA2;
-  constexpr int C1 = CA1 + 3, C2 = CA2 + 2, C3 = CA3 + 3;
+  constexpr int NC = NA + 8;           // copy instructions per wavefront and slab
+  constexpr int C12 = (2 * NC + 2) / 3;  // of them issued in phases 2 and 3 (see copy_pos)
   __shared__ __attribute__((aligned(1024))) uint16_t a0[kGemmHalf];
   __shared__ __attribute__((aligned(1024))) uint16_t b0[kGemmHalf];
   __shared__ __attribute__((aligned(1024))) uint16_t a1[kGemmHalf];
@@ -355,6 +355,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
       issue_b(kt, sb, i);
     }
   };
+  // Copy c (0 .. NC-1) of a slab: the A and B instructions of i = c / 2 alternately while
+  // i < NA, then the remaining B instructions.
+  auto copy1 = [&](int kt, uint16_t* sa, uint16_t* sb, int c) __attribute__((always_inline)) {
+    if (c < 2 * NA) {
+      if (c & 1) issue_b(kt, sb, c >> 1);
+      else issue_a(kt, sa, c >> 1);
+    } else {
+      issue_b(kt, sb, c - NA);
+    }
+  };
 
   // Fragment reads (16x16x32 operands): lane l reads row 16 * block + l % 16, the 8 k of
   // logical chunk 4 ks + l / 16 of k-step ks, at physical chunk (4 ks + l / 16) ^ ((l % 16 >> 1) & 7);
@@ -386,8 +396,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   };
   // One phase: the P MFMAs of k-step buf over fragment rows [h MI/2, (h+1) MI/2) (all NJ column
   // blocks), with fragment read x (x < nr: k-step rks of stage (rsa, rsb) into buffer rbuf)
-  // and copy slot x (copies i0 .. i1-1 of slab tc into stage (wa, wb): even slots the A
-  // instruction of i0 + x/2 when it exists, odd slots its B instruction) behind MFMA x.
+  // behind MFMA x.  In copy phase cq (1..3; 0: none) the copies of slab tc into stage (wa, wb)
+  // are spread evenly: copy c goes behind MFMA position copy_pos(c) = c * 3P / NC of the three
+  // phases' 3P MFMAs.  A CU's load path moves about 64 bytes per clock, so the 4 KiB that four
+  // wavefronts' copies carry per MFMA position must not come in bursts: a wavefront whose copy
+  // cannot issue holds back the MFMAs behind it.
   //
   // The MFMA is written as inline asm with its accumulator tied ("+a"): the builtin's untied
   // 16x16 form lets the register allocator rotate the accumulators through copies on every
@@ -396,17 +409,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   // the accumulators (the fragment registers a read overwrites were last read at least 8
   // MFMAs earlier): the zeroing before the first MFMA and the epilogue's reads after the last
   // one are separated from them by explicit wait states.
-  auto phase = [&](int buf, int h, int nr, int rbuf, const uint16_t* rsa, const uint16_t* rsb, int rks, int tc,
-                   uint16_t* wa, uint16_t* wb, int i0, int i1) __attribute__((always_inline)) {
+  auto phase = [&](int buf, int h, int nr, int rbuf, const uint16_t* rsa, const uint16_t* rsb, int rks, int cq, int tc,
+                   uint16_t* wa, uint16_t* wb) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < P; ++x) {
       const int i = h * (MI / 2) + x / NJ, j = x % NJ;
       asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fb[buf][j]), "v"(fa[buf][i]));
       if (x < nr) rd1(rbuf, rsa, rsb, rks, x);
-      const int ci = i0 + x / 2;
-      if (ci < i1) {
-        if (x & 1) issue_b(tc, wb, ci);
-        else if (ci < NA) issue_a(tc, wa, ci);
+      if (cq > 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          if (c * 3 * P / NC == (cq - 1) * P + x) copy1(tc, wa, wb, c);
       }
     }
   };
@@ -416,21 +429,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   // each in two halves of its fragment rows.
   //   1: k-step 1's fragments are read behind the first NR MFMAs; then the stage is consumed
   //      (own reads waited for, a barrier for everyone's) and is free for slab t+2;
-  //   2, 3: the copies of slab t+2 (instructions 0..2, then 3..4), spread over the MFMAs;
+  //   2, 3: copies 0 .. C12-1 of slab t+2 spread over the MFMAs;
   //   before 4: this wave's copies of slab t+1 landed, a barrier: slab t+1 is complete;
-  //   4: copies 5..7 and the reads of slab t+1's k-step 0 fragments behind the MFMAs.
+  //   4: the rest of the copies, and the reads of slab t+1's k-step 0 fragments behind the
+  //      MFMAs.
   auto slab = [&](int t, const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb) __attribute__((always_inline)) {
     uint16_t* wa = const_cast<uint16_t*>(ca);
     uint16_t* wb = const_cast<uint16_t*>(cb);
     const int tc = min(t + 2, ke - 1);  // branch-free: past the end the last slab is fetched again
-    phase(0, 0, NR, 1, ca, cb, 1, tc, wa, wb, 0, 0);
+    phase(0, 0, NR, 1, ca, cb, 1, 0, tc, wa, wb);
     wait_lgkm0();   // own reads of this stage done
     lds_barrier();  // everyone's: the stage is free
-    phase(0, 1, 0, 0, ca, cb, 0, tc, wa, wb, 0, 3);
-    phase(1, 0, 0, 0, ca, cb, 0, tc, wa, wb, 3, 5);
-    wait_vm_lgkm0<C1 + C2>();  // own copies of slab t+1 landed (those of slab t+2 may be in flight)
-    lds_barrier();             // everyone's: slab t+1 is complete
-    phase(1, 1, NR, 0, na, nb, 0, tc, wa, wb, 5, 8);
+    phase(0, 1, 0, 0, ca, cb, 0, 1, tc, wa, wb);
+    phase(1, 0, 0, 0, ca, cb, 0, 2, tc, wa, wb);
+    wait_vm_lgkm0<C12>();  // own copies of slab t+1 landed (those of slab t+2 may be in flight)
+    lds_barrier();         // everyone's: slab t+1 is complete
+    phase(1, 1, NR, 0, na, nb, 0, 3, tc, wa, wb);
   };
 
   issue(kb, a0, b0, 0, 8);
