@@ -262,7 +262,9 @@ typedef struct {
  * (PBLOCK_ERR_NULL).  Switch values other than 0/1, or a bad rope_base, give
  * PBLOCK_ERR_ARG.  With rope = 1 the cos/sin table for positions [0, B*S of the create
  * cfg) is built in the handle's workspace (fp64, rounded to fp32) on `stream` the first
- * time a base is used, and again whenever the base changes.  With two_ln = 1 the input
+ * time a base is used, and again whenever the base changes or the call comes on another
+ * stream than the one the table was last built on (so a call never relies on work enqueued
+ * on a different stream; calls on one handle must still not overlap).  With two_ln = 1 the input
  * GEMM runs as two launches around the second LayerNorm.  Stream, ownership, alignment,
  * aliasing (out must not overlap the extra parameters either) and cfg rules as
  * pblock_forward; per-kernel timing covers it like pblock_forward (a second LayerNorm

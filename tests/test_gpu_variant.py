@@ -142,6 +142,32 @@ def test_rope_base_change_rebuilds_table():
         tb.pblock_destroy(h)
 
 
+def test_rope_on_a_second_stream():
+    """Rotary calls on one handle from two streams in turn (each synchronised before the next):
+    the table is rebuilt on the second stream, and both results equal the oracle's and each other."""
+    import torch
+
+    import transformer_block_fwd_amd as tb
+
+    cfg = BlockConfig("rope_streams", B=1, S=193, d=256, H=2, hd=64, ffn=128, W=64, dtype="bf16")
+    inp = make_inputs(cfg, seed=29, affine=True)
+    dev = upload(inp)
+    ref = oracle.block_forward_variant(inp.x, inp.gamma, inp.beta, inp.w_in, inp.w_out, cfg.H, cfg.hd, cfg.W,
+                                       eps=cfg.ln_eps, rope_base=10000.0)
+    h = tb.pblock_create(cfg)
+    s2 = torch.cuda.Stream()
+    try:
+        y1 = run_variant(cfg, dev, None, dict(rope=True, rope_base=10000.0), handle=h)
+        with torch.cuda.stream(s2):
+            y2 = run_variant(cfg, dev, None, dict(rope=True, rope_base=10000.0), handle=h)
+        y3 = run_variant(cfg, dev, None, dict(rope=True, rope_base=10000.0), handle=h)
+        for y in (y1, y2, y3):
+            assert rel_err(y, ref) <= TOL["bf16"]
+        assert np.array_equal(y1, y2) and np.array_equal(y1, y3)
+    finally:
+        tb.pblock_destroy(h)
+
+
 def test_variant_rejections_leave_out_untouched():
     import torch
 

@@ -445,7 +445,8 @@ struct pblock_s {
   size_t ev_used;
   double ms_sum[kTimedKernels];
   int n_forwards;
-  double rope_base;  // base the rotary table in the workspace was built for (NaN: none yet)
+  double rope_base;         // base the rotary table in the workspace was built for (NaN: none yet)
+  hipStream_t rope_stream;  // stream it was built on (a call on another stream rebuilds it there)
 };
 
 namespace {
@@ -814,6 +815,7 @@ int pblock_create(const pblock_cfg* cfg, pblock_t* out_handle) {
     h->ev_used = 0;
     h->n_forwards = 0;
     h->rope_base = std::nan("");
+    h->rope_stream = nullptr;
     for (double& v : h->ms_sum) v = 0.0;
     hipError_t e = hipMalloc(&h->ws, size_t(h->lay.total));
     if (e != hipSuccess) {
@@ -1192,14 +1194,17 @@ int pblock_forward_variant(pblock_t h, const void* x, const pblock_weights* w, c
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Ws ws = workspace(h);
     const int64_t A = dm.A;
-    if (v.rope && !(double(v.rope_base) == h->rope_base)) {
-      // (cos, sin) for every position the handle can see; rebuilt only when the base changes
+    if (v.rope && (!(double(v.rope_base) == h->rope_base) || s != h->rope_stream)) {
+      // (cos, sin) for every position the handle can see; rebuilt when the base changes, and
+      // on the calling stream whenever it is not the stream the table was built on, so that
+      // every call reads a table its own stream ordered before it
       const int64_t n = h->m_cap * (c.hd / 2);
       hipLaunchKernelGGL(rope_table_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, ws.rope, int(h->m_cap),
                          c.hd, double(v.rope_base));
       st = launch_status("rope table launch");
       if (st != PBLOCK_OK) return st;
       h->rope_base = double(v.rope_base);
+      h->rope_stream = s;
     }
     Timer tm;
     st = tm.begin(h, s);
