@@ -272,6 +272,27 @@ def test_attention_entry_point(hd):
         assert err <= TOL["bf16"], (S, W)
 
 
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("H", [2, 512], ids=["few_heads", "many_heads"])
+def test_attention_both_forms(H, hd):
+    """Both attention forms against the oracle: with 2 heads the launch has fewer 128-query
+    workgroups than twice the CUs and runs the 64-query form; with 512 heads it has more and
+    runs the 128-query form.  Ragged S, a window that is not a multiple of the key tile."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    B, S, W = 1, 300, 65
+    A = H * hd
+    qkv = (rng.standard_normal((B * S, 3 * A), dtype=np.float32) * 1.5).astype(np.float32)
+    qkv_t = torch.from_numpy(qkv).cuda().to(torch.bfloat16)
+    o = torch.zeros((B * S, A), dtype=torch.bfloat16, device="cuda")
+    tb.pblock_swa_attention(qkv_t, 3 * A, o, A, B, S, H, hd, W, "bf16")
+    torch.cuda.synchronize()
+    qv = from_dev(qkv_t).reshape(S, 3, H, hd)
+    ref = oracle.swa_attention(qv[:, 0], qv[:, 1], qv[:, 2], W)
+    err = rel_err(from_dev(o).reshape(S, H, hd), ref)
+    log(f"[parity] attention H={H} hd={hd}: {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_attention_entry_fp32():
     rng = np.random.Generator(np.random.PCG64(11))
     B, S, H, hd, W = 1, 200, 2, 64, 33
