@@ -274,10 +274,9 @@ def test_attention_entry_point(hd):
 
 @pytest.mark.parametrize("hd", [64, 128])
 @pytest.mark.parametrize("H", [2, 512], ids=["few_heads", "many_heads"])
-def test_attention_both_forms(H, hd):
-    """Both attention forms against the oracle: with 2 heads the launch has fewer 128-query
-    workgroups than twice the CUs and runs the 64-query form; with 512 heads it has more and
-    runs the 128-query form.  Ragged S, a window that is not a multiple of the key tile."""
+def test_attention_head_counts(H, hd):
+    """Few and many heads (a launch under one workgroup per CU, and one of several waves of
+    them) against the oracle; ragged S, a window that is not a multiple of the key tile."""
     rng = np.random.Generator(np.random.PCG64(12))
     B, S, W = 1, 300, 65
     A = H * hd

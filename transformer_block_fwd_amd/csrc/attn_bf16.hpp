@@ -321,243 +321,3 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
 }
 
 }  // namespace pblk
-
-namespace pblk {
-
-// Small-grid form of the same attention: one workgroup = one (sequence, head, 64-query
-// tile), four wavefronts of 16 queries each, on the 16x16x32 bf16 MFMA.  It is launched when
-// the 128-query form would give fewer than two workgroups per compute unit (the 175B shard's
-// 12 local heads x 16 tiles = 192 on 256 CUs): with half the queries per wavefront there are
-// twice the wavefronts, so every CU is used and two of them can share a SIMD, one's softmax
-// arithmetic running while the other's MFMAs do.  K/V tiles, their copies and LDS layouts,
-// the band walk and the online softmax are the 128-query kernel's.
-//
-// S^T = K Q^T per 16-key block kb: the key fragment (16 keys x 32 of the head dimension) is
-// the first operand, the query fragment (kept in registers) the second, so lane l owns query
-// l % 16 and keys 16 kb + 4 (l / 16) + 0..3.  For O^T = V^T P^T a 32-key chunk c is one
-// MFMA: P's operand gives lane l the keys {32c + 4g + e, 32c + 16 + 4g + e : e < 4}, g = l / 16,
-// exactly its scores of blocks 2c and 2c + 1, and the V^T fragment (16 head-dim columns x the
-// same 8 keys per lane group) comes from two transpose reads whose 16-lane group g addresses
-// key rows 32c + 4g + j / 4 (and 16 further) at columns 16 hb + 4 (j % 4): lane j of the group
-// receives column 16 hb + j of those four keys.  The row max and sum of a query span the four
-// lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48).
-constexpr int kAttnBQ16 = 64;
-
-// v combined with the values the other three 16-lane groups hold at the same lane % 16
-__device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, other_half(v));
-}
-__device__ __forceinline__ float group4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + other_half(v);
-}
-
-template <int HD>
-__global__ __launch_bounds__(kAttnThreads, 2) void swa_attn16_bf16_kernel(AttnArgs a) {
-  constexpr int BQ = kAttnBQ16, BKV = kAttnBKV;
-  constexpr int NW = kAttnThreads / 64;
-  constexpr int ROWB = HD * 2;         // bytes per K/V row
-  constexpr int TB = BKV * ROWB;       // bytes per K or V tile
-  constexpr int NI = TB / 1024;        // 1 KiB copy instructions per tile
-  constexpr int NIW = NI / NW;         // ... issued by each wave
-  constexpr int NKS = HD / 32;         // 32-deep slices of the QK^T contraction
-  constexpr int NHB = HD / 16;         // 16-wide head-dim blocks of the output
-  static_assert(NIW * NW == NI, "copy instructions split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t k_st0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_st0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_st1[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_st1[TB];
-
-  const int S = a.S, W = a.W;
-  const int nqt = (a.q_hi - a.q_lo + BQ - 1) / BQ;
-  const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int qt = nqt - 1 - blockIdx.x / BH;
-  const int b = bh / a.H, h = bh % a.H;
-  const int A = a.H * HD;
-  const uint16_t* qbase = a.qkv + int64_t(b) * S * a.ld_qkv + h * HD;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(qbase + A);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(qbase + 2 * A);
-  const uint32_t ldb = uint32_t(a.ld_qkv) * 2u;  // row pitch in bytes
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy targets in SGPRs
-  const int lr = lane & 15, lg = lane >> 4;
-  const int q0 = a.q_lo + qt * BQ;
-  const int wq0 = q0 + wave * 16;
-  const int my_q = wq0 + lr;
-
-  bf16x8 qf[NKS];
-  {
-    const uint16_t* qp = qbase + int64_t(min(my_q, S - 1)) * a.ld_qkv + lg * 8;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
-  }
-
-  const int q_last = min(q0 + BQ, a.q_hi) - 1;
-  const int t_begin = max(0, q0 - W + 1) / BKV;
-  const int t_end = q_last / BKV;
-
-  // Copies: the 128-query kernel's (instruction c of this wave fills LDS bytes
-  // [1024 i, 1024 i + 1024) of a tile, i = wave * NIW + c).
-  auto copy_row = [&](int c) { return (1024 * (wave * NIW + c) + 16 * lane) / ROWB; };
-  auto copy_pc = [&](int c) { return ((16 * lane) % ROWB) / 16; };
-  static_assert(NIW <= 4 && NKS <= 4 && NHB <= 8, "offset arrays sized for hd <= 128");
-  uint32_t koff[4], voff[4];
-#pragma unroll
-  for (int c = 0; c < NIW; ++c) {
-    const int r = copy_row(c), pc = copy_pc(c);
-    koff[c] = uint32_t(r) * ldb + uint32_t((pc ^ swz_k<HD>(r)) << 4);
-    voff[c] = uint32_t(r) * ldb + uint32_t((pc ^ swz_v<HD>(r)) << 4);
-  }
-  // key rows at or past q_hi are clamped to q_hi - 1 (see the 128-query kernel)
-  const int kv_end = a.q_hi;
-  auto issue = [&](int t, uint8_t* ks, uint8_t* vs) {
-    const int j0 = t * BKV;
-    const uint8_t* kt = kbase + int64_t(j0) * ldb;
-    const uint8_t* vt = vbase + int64_t(j0) * ldb;
-    if (j0 + BKV <= kv_end) {
-#pragma unroll
-      for (int c = 0; c < NIW; ++c) {
-        __builtin_amdgcn_global_load_lds(kt + koff[c], (lds_void*)(ks + 1024 * (wave * NIW + c)), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + voff[c], (lds_void*)(vs + 1024 * (wave * NIW + c)), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < NIW; ++c) {
-        const int r = copy_row(c), pc = copy_pc(c);
-        const uint32_t rb = uint32_t(min(j0 + r, kv_end - 1) - j0) * ldb;
-        __builtin_amdgcn_global_load_lds(kt + rb + uint32_t((pc ^ swz_k<HD>(r)) << 4),
-                                         (lds_void*)(ks + 1024 * (wave * NIW + c)), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + rb + uint32_t((pc ^ swz_v<HD>(r)) << 4),
-                                         (lds_void*)(vs + 1024 * (wave * NIW + c)), 16, 0, 0);
-      }
-    }
-  };
-
-  // Fragment read offsets within a tile.  K: row 16 kb + lr, logical chunk 4 ks + lg (the
-  // swizzle depends on row % 16 only, so kb adds a plain 16 rows).  V (transpose read): lane
-  // 16 lg + j addresses key row 4 lg + j / 4 (+ 32 c, + 16 for the second read) and the
-  // 8-byte piece at head-dim column 16 hb + 4 (j % 4).
-  uint32_t kro[NKS], vro[NHB];
-  {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kro[ks] = uint32_t(lr * ROWB + (((4 * ks + lg) ^ swz_k<HD>(lr)) << 4));
-    const int j = lane & 15;
-    const int vrow = 4 * lg + (j >> 2);
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      const int col = 16 * hb + 4 * (j & 3);  // first of the piece's four columns
-      vro[hb] = uint32_t(vrow * ROWB + (((col >> 3) ^ swz_v<HD>(vrow)) << 4) + (col & 7) * 2);
-    }
-  }
-
-  f32x4 oacc[NHB];
-#pragma unroll
-  for (int t = 0; t < NHB; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;  // m_run: reference max in log2 units
-
-  auto compute = [&](int t, const uint8_t* ks, const uint8_t* vs) {
-    const int j0 = t * BKV;
-    const bool active = (wq0 < a.q_hi) && (j0 <= wq0 + 15) && (j0 + BKV - 1 >= wq0 - W + 1);
-    if (!active) return;
-    f32x4 sacc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < NKS; ++q) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kro[q] + kb * 16 * ROWB);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[q], sacc[kb], 0, 0, 0);
-      }
-    }
-    // lane owns query my_q and keys j0 + 16 kb + 4 lg + r; in the band iff 0 <= my_q - j < W
-    const bool full = (j0 + BKV - 1 <= wq0) && (j0 >= wq0 + 15 - W + 1);
-    if (!full) {
-      const int diff = my_q - j0 - 4 * lg;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sacc[kb][r] = (uint32_t(diff - (16 * kb + r)) < uint32_t(W)) ? sacc[kb][r] : -INFINITY;
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
-    const float m_tile = group4_max(mloc) * a.scale_log2;
-    // lazy rescaling as in the 128-query kernel
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
-      m_run = m_new;
-      l_part *= alpha;
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) oacc[hb] *= alpha;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    // P in bf16 as the B operand of O^T = V^T P^T, chunk c = blocks 2c and 2c + 1; the row sum
-    // adds the rounded weights the product uses
-    bf16x8 pf[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x2 w[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int kb = 2 * c + (e2 >> 1), r = 2 * (e2 & 1);
-        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.scale_log2, -m_use)),
-                          __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], a.scale_log2, -m_use))};
-        w[e2] = __builtin_convertvector(pp, bf16x2);
-        l_part = __builtin_amdgcn_fdot2_f32_bf16(w[e2], kOnesBf16x2, l_part, false);
-      }
-      pf[c] = bf16x8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
-    }
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint8_t* p = vs + vro[hb] + c * 32 * ROWB;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * ROWB));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 u = {lo2.x, lo2.y, hi2.x, hi2.y};
-        oacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pf[c], oacc[hb], 0, 0, 0);
-      }
-  };
-
-  // the 128-query kernel's two-stage loop
-  auto step = [&](int t, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn) {
-    attn_wait_copies();
-    attn_barrier();
-    if (t < t_end) issue(t + 1, kn, vn);
-    compute(t, ks, vs);
-  };
-  issue(t_begin, k_st0, v_st0);
-  const int n_tiles = t_end - t_begin + 1;
-  int t = t_begin;
-  for (int p = 0; p + 2 <= n_tiles; p += 2, t += 2) {
-    step(t, k_st0, v_st0, k_st1, v_st1);
-    step(t + 1, k_st1, v_st1, k_st0, v_st0);
-  }
-  if (n_tiles & 1) step(t, k_st0, v_st0, k_st1, v_st1);
-
-  const float l = group4_sum(l_part);
-  if (my_q < a.q_hi) {
-    if (a.lse != nullptr && lg == 0)
-      a.lse[(int64_t(b) * a.H + h) * S + my_q] = ((m_run == -INFINITY) ? 0.f : m_run) + log2f(l);
-    const float inv = 1.0f / l;
-    uint16_t* orow = a.o + (int64_t(b) * S + my_q) * a.ld_o + h * HD;
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      const f32x2 p0 = {oacc[hb][0] * inv, oacc[hb][1] * inv};
-      const f32x2 p1 = {oacc[hb][2] * inv, oacc[hb][3] * inv};
-      const u32x2 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(p0, bf16x2)),
-                       __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, bf16x2))};
-      *reinterpret_cast<u32x2*>(orow + 16 * hb + 4 * lg) = w;
-    }
-  }
-}
-
-}  // namespace pblk

@@ -112,7 +112,6 @@ WsLayout ws_layout(const pblock_cfg* c, int G) {
 // Per-device cache of "is this a gfx950": 0 unknown, 1 yes, -1 no (threads may fill it
 // concurrently; they all store the same value).
 std::atomic<int> g_arch_ok[64];
-std::atomic<int> g_dev_cus[64];  // compute units per device (0 unknown)
 
 int check_device(int* dev_out) {
   int dev = -1;
@@ -123,7 +122,6 @@ int check_device(int* dev_out) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(PBLOCK_ERR_DEVICE, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
-    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_arch_ok[dev].store((std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1, std::memory_order_relaxed);
   }
   if (g_arch_ok[dev].load(std::memory_order_relaxed) != 1) return fail(PBLOCK_ERR_DEVICE, "current device is not gfx950");
@@ -405,19 +403,9 @@ void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, in
     a.B = B; a.S = S; a.H = H; a.W = W;
     a.q_lo = q_lo; a.q_hi = q_hi;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const int64_t grid = ((q_hi - q_lo + kAttnBQ - 1) / kAttnBQ) * int64_t(B) * H;
-    // fewer than two 128-query workgroups per CU: the 64-query form (twice the wavefronts)
-    int dev = 0;
-    const int cus = (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) ? g_dev_cus[dev].load() : 0;
-    if (grid < 2 * int64_t(cus)) {
-      const unsigned g16 = unsigned(((q_hi - q_lo + kAttnBQ16 - 1) / kAttnBQ16) * int64_t(B) * H);
-      if (hd == 128) hipLaunchKernelGGL((swa_attn16_bf16_kernel<128>), dim3(g16), dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((swa_attn16_bf16_kernel<64>), dim3(g16), dim3(256), 0, s, a);
-    } else if (hd == 128) {
-      hipLaunchKernelGGL((swa_attn_bf16_kernel<128>), dim3(unsigned(grid)), dim3(256), 0, s, a);
-    } else {
-      hipLaunchKernelGGL((swa_attn_bf16_kernel<64>), dim3(unsigned(grid)), dim3(256), 0, s, a);
-    }
+    const unsigned grid = unsigned(((q_hi - q_lo + kAttnBQ - 1) / kAttnBQ) * int64_t(B) * H);
+    if (hd == 128) hipLaunchKernelGGL((swa_attn_bf16_kernel<128>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((swa_attn_bf16_kernel<64>), dim3(grid), dim3(256), 0, s, a);
   } else {
     const dim3 grid{unsigned(int64_t((q_hi - q_lo + 63) / 64) * H * B)};
     const float* q = static_cast<const float*>(qkv);
