@@ -15,7 +15,11 @@ namespace pblk {
 template <int EPI, bool AK>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g, GemmSched sk) {
   constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, NT = kGemmThreads;
-  constexpr int FM = 4, FN = 4;  // 32x32 MFMA tiles per wavefront (128 x 128)
+  constexpr int MI = 8, NJ = 8;   // 16x16 MFMA tiles per wavefront (128 x 128)
+  constexpr int P = MI * NJ / 2;  // MFMAs per phase (half a 32-deep k-step)
+  constexpr int NRF = MI + NJ;    // operand fragments per k-step
+  constexpr int NC = 16;          // copy instructions per wavefront and slab (8 per operand)
+  constexpr int C12 = (2 * NC + 2) / 3;  // of them issued in phases 2 and 3
   __shared__ __attribute__((aligned(1024))) uint16_t a0[kGemmHalf];
   __shared__ __attribute__((aligned(1024))) uint16_t b0[kGemmHalf];
   __shared__ __attribute__((aligned(1024))) uint16_t a1[kGemmHalf];
@@ -25,7 +29,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lg = lane >> 5;
 
   int L, kb, ke, tl = -1, chunk = 0;
   if (int(blockIdx.x) < sk.dp_units) {
@@ -64,132 +67,130 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g
     }
   }
   const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(g.a) + (AK ? int64_t(0) : int64_t(m0 + wave * 64) * lda_b);
+  // copy instruction i (0..7) of slab kt, A or B
+  auto issue_a = [&](int kt, uint16_t* sa, int i) __attribute__((always_inline)) {
+    const int64_t krow0 = int64_t(kt) * BK + 16 * wave + 2 * i;  // K-major: first k row of the block
+    const uint8_t* ga = AK ? a_blk + krow0 * lda_b + offa[i & 1]
+                           : a_blk + int64_t(8 * i) * lda_b + uint32_t(kt) * (BK * 2) + offa[i & 1];
+    __builtin_amdgcn_global_load_lds(ga, (PBLK_LDS void*)(sa + (wave * 8 + i) * 512), 16, 0, 0);
+  };
+  auto issue_b = [&](int kt, uint16_t* sb, int i) __attribute__((always_inline)) {
+    const int64_t krow0 = int64_t(kt) * BK + 16 * wave + 2 * i;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(g.b) + krow0 * ldb_b + offb[i & 1],
+                                     (PBLK_LDS void*)(sb + (wave * 8 + i) * 512), 16, 0, 0);
+  };
   auto issue = [&](int kt, uint16_t* sa, uint16_t* sb, int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      const int64_t krow0 = int64_t(kt) * BK + 16 * wave + 2 * i;  // K-major: first k row of the block
-      const uint8_t* ga = AK ? a_blk + krow0 * lda_b + offa[i & 1]
-                             : a_blk + int64_t(8 * i) * lda_b + uint32_t(kt) * (BK * 2) + offa[i & 1];
-      __builtin_amdgcn_global_load_lds(ga, (PBLK_LDS void*)(sa + (wave * 8 + i) * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(g.b) + krow0 * ldb_b + offb[i & 1],
-                                       (PBLK_LDS void*)(sb + (wave * 8 + i) * 512), 16, 0, 0);
+      issue_a(kt, sa, i);
+      issue_b(kt, sb, i);
     }
   };
 
-  // Fragment reads.  Row-major A: row w*128 + i*32 + lr, logical chunk 2kk + lg at physical
-  // (2kk + lg) ^ ((lr >> 1) & 7).  K-major operand tile t (m or n = w*128 + t*32 + lane%32):
-  // two transpose reads (ds_read_b64_tr_b16) in which lane 16G + j addresses k row
-  // kk*16 + 8*(G/2) + j/4 (+4 for the second) and columns w*128 + t*32 + 16*(G%2) + 4*(j%4) .. +3,
-  // so lane L receives k = kk*16 + 8*(L/32) + 0..3 (then 4..7) of column L%32: the MFMA operand.
-  uint32_t rda[4], trb[4], tra[4];
+  // Fragment reads (16x16x32 operands: lane l holds row or column 16 * block + l % 16 and the
+  // 8 k of k-group l / 16 of a 32-deep k-step ks).  Row-major A: row w*128 + 16 i + l % 16,
+  // logical chunk 4 ks + l / 16 at physical chunk (4 ks + l / 16) ^ ((l % 16 >> 1) & 7).
+  // K-major operand block t (m or n = w*128 + 16 t + l % 16): two transpose reads
+  // (ds_read_b64_tr_b16) in which lane 16G + j addresses k row 32 ks + 8 G + j / 4 (+4 for the
+  // second) and columns w*128 + 16 t + 4 (j % 4) .. +3, so lane 16G + j receives k =
+  // 32 ks + 8 G + 0..3 (then 4..7) of column 16 t + j: the MFMA operand.
+  const int lr = lane & 15, lq = lane >> 4;
+  uint32_t rda[2], trb, tra;
   {
     const int G = lane >> 4, j = lane & 15;
-    const int krow = 8 * (G >> 1) + (j >> 2);
-    const int sw = 4 * ((j >> 2) & 3);
+    const int krow = 8 * G + (j >> 2);
+    const int sw = 4 * ((j >> 2) & 3);            // 4 * (krow & 3)
+    const int cb = (wn * 128 + 4 * (j & 3)) >> 3;  // logical chunk of the first column
+    const int ca = (wm * 128 + 4 * (j & 3)) >> 3;
+    trb = uint32_t(krow * 512 + (((cb) ^ sw) << 4) + 8 * (j & 1));
+    tra = uint32_t(krow * 512 + (((ca) ^ sw) << 4) + 8 * (j & 1));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int e = 2 * (G & 1) + ((j & 3) >> 1);
-      trb[t] = uint32_t(krow * 512 + (((wn * 16 + 4 * t + e) ^ sw) << 4) + 8 * (j & 1));
-      tra[t] = uint32_t(krow * 512 + (((wm * 16 + 4 * t + e) ^ sw) << 4) + 8 * (j & 1));
-      rda[t] = uint32_t(lr * 128 + (((2 * t + lg) ^ ((lr >> 1) & 7)) << 4)) + uint32_t(wm * 128 * 128);
-    }
+    for (int ks = 0; ks < 2; ++ks)
+      rda[ks] = uint32_t(lr * 128 + (((4 * ks + lq) ^ ((lr >> 1) & 7)) << 4)) + uint32_t(wm * 128 * 128);
   }
 
-  f32x16 acc[FM][FN];
+  f32x4 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 fa[4][FM], fb[4][FN];  // one fragment buffer per k-step of a slab
-  auto trfrag = [&](const uint8_t* p) __attribute__((always_inline)) {
+  bf16x8 fa[2][MI], fb[2][NJ];  // one fragment buffer per k-step of a slab
+  // the K-major fragment of block t (16 columns) of k-step ks: the physical chunk of column
+  // 16 t + c0 is (logical + 2t) ^ sw, the XOR touching only bits 2..3 of the chunk index
+  auto trfrag = [&](const uint8_t* base, uint32_t off, int t, int ks) __attribute__((always_inline)) {
+    const uint8_t* p = base + (off ^ uint32_t((2 * t) << 4)) + ks * 32 * 512;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * 512));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     const u32x4 u = {l2.x, l2.y, h2.x, h2.y};
     return __builtin_bit_cast(bf16x8, u);
   };
-  auto rd = [&](int buf, const uint16_t* sa, const uint16_t* sb, int kk) __attribute__((always_inline)) {
+  // fragment x (0 .. NRF-1) of k-step ks into buffer buf, in the order the MFMAs consume them:
+  // A block 0, B blocks 0 .. NJ-1, A blocks 1 .. MI-1
+  auto rd1 = [&](int buf, const uint16_t* sa, const uint16_t* sb, int ks, int x) __attribute__((always_inline)) {
     const uint8_t* pa = reinterpret_cast<const uint8_t*>(sa);
     const uint8_t* pb = reinterpret_cast<const uint8_t*>(sb);
-    // in the order the MFMAs consume them
-    if constexpr (AK) fa[buf][0] = trfrag(pa + tra[0] + kk * 16 * 512);
-    else fa[buf][0] = *reinterpret_cast<const bf16x8*>(pa + rda[kk]);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[buf][j] = trfrag(pb + trb[j] + kk * 16 * 512);
-#pragma unroll
-    for (int i = 1; i < FM; ++i) {
-      if constexpr (AK) fa[buf][i] = trfrag(pa + tra[i] + kk * 16 * 512);
-      else fa[buf][i] = *reinterpret_cast<const bf16x8*>(pa + rda[kk] + i * 32 * 128);
+    const bool is_b = x >= 1 && x <= NJ;
+    const int blk = is_b ? x - 1 : (x == 0 ? 0 : x - NJ);
+    if (is_b) {
+      fb[buf][blk] = trfrag(pb, trb, blk, ks);
+    } else if constexpr (AK) {
+      fa[buf][blk] = trfrag(pa, tra, blk, ks);
+    } else {
+      fa[buf][blk] = *reinterpret_cast<const bf16x8*>(pa + rda[ks] + blk * 16 * 128);
     }
   };
-  auto mm = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  // copy c (0 .. NC-1): the A and B instructions of i = c / 2 alternately
+  auto copy1 = [&](int kt, uint16_t* sa, uint16_t* sb, int c) __attribute__((always_inline)) {
+    if (c & 1) issue_b(kt, sb, c >> 1);
+    else issue_a(kt, sa, c >> 1);
   };
-  // sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read
-  // LDS read instructions per k-step: 4 (row-major A) or 8 (K-major A) plus 8 for K-major B
-  constexpr int RD = (AK ? 8 : 4) + 8;
-  // 16 MFMAs with the 3 * RD fragment reads of the next three k-steps behind the first 12
-  auto interleave_rd24 = [&]() __attribute__((always_inline)) {
+  // One phase, as in the forward GEMM: the P MFMAs of k-step buf over fragment rows
+  // [h MI/2, (h+1) MI/2), fragment read x behind MFMA x (x < nr), and in copy phase cq (1..3)
+  // copy c behind MFMA position c * 3P / NC of the three phases.  Tied inline-asm MFMAs (see
+  // gemm_bf16.hpp): memory operations keep their program order around them.
+  auto phase = [&](int buf, int h, int nr, int rbuf, const uint16_t* rsa, const uint16_t* rsb, int rks, int cq, int tc,
+                   uint16_t* wa, uint16_t* wb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < 12; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, RD / 4, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  };
-  // 16 MFMAs with n copy instructions and nr fragment reads spread over them
-  auto interleave_cp = [&](int n, int nr) __attribute__((always_inline)) {
+    for (int x = 0; x < P; ++x) {
+      const int i = h * (MI / 2) + x / NJ, j = x % NJ;
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fb[buf][j]), "v"(fa[buf][i]));
+      if (x < nr) rd1(rbuf, rsa, rsb, rks, x);
+      if (cq > 0) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (x < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (x < n) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        for (int c = 0; c < NC; ++c)
+          if (c * 3 * P / NC == (cq - 1) * P + x) copy1(tc, wa, wb, c);
+      }
     }
   };
 
   // Slab t in stage (ca, cb), its k-step 0 fragments requested into buffer 0, the copies of
-  // slab t+1 into stage (na, nb) in flight.
+  // slab t+1 into stage (na, nb) in flight: the forward GEMM's four phases.
   auto slab = [&](int t, const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb) __attribute__((always_inline)) {
     uint16_t* wa = const_cast<uint16_t*>(ca);
     uint16_t* wb = const_cast<uint16_t*>(cb);
     const int tc = min(t + 2, ke - 1);  // branch-free: past the end the last slab is fetched again
-    rd(1, ca, cb, 1);
-    rd(2, ca, cb, 2);
-    rd(3, ca, cb, 3);
-    mm(0);
-    interleave_rd24();
-    __builtin_amdgcn_sched_barrier(0);
+    phase(0, 0, NRF, 1, ca, cb, 1, 0, tc, wa, wb);
     wait_lgkm0();   // own reads of this stage done
     lds_barrier();  // everyone's: the stage is free
-    issue(tc, wa, wb, 0, 3);
-    mm(1);
-    interleave_cp(6, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(tc, wa, wb, 3, 5);
-    mm(2);
-    interleave_cp(4, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm_lgkm0<10>();  // own copies of slab t+1 landed (10 of slab t+2 may be in flight)
-    lds_barrier();        // everyone's: slab t+1 is complete
-    issue(tc, wa, wb, 5, 8);
-    rd(0, na, nb, 0);
-    mm(3);
-    interleave_cp(6, RD > 16 ? 16 : RD);
-    __builtin_amdgcn_sched_barrier(0);
+    phase(0, 1, 0, 0, ca, cb, 0, 1, tc, wa, wb);
+    phase(1, 0, 0, 0, ca, cb, 0, 2, tc, wa, wb);
+    wait_vm_lgkm0<C12>();  // own copies of slab t+1 landed (those of slab t+2 may be in flight)
+    lds_barrier();         // everyone's: slab t+1 is complete
+    phase(1, 1, NRF, 0, na, nb, 0, 3, tc, wa, wb);
   };
 
   issue(kb, a0, b0, 0, 8);
   issue(min(kb + 1, ke - 1), a1, b1, 0, 8);
   wait_vm_lgkm0<16>();  // slab kb landed
   lds_barrier();
-  rd(0, a0, b0, 0);
+#pragma unroll
+  for (int x = 0; x < NRF; ++x) rd1(0, a0, b0, 0, x);
+  // the accumulators' zeroing (VALU writes) before their first MFMA read
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 4");
+  __builtin_amdgcn_sched_barrier(0);
   const int n = ke - kb;
   int kt = kb;
   for (int p = 0; p + 2 <= n; p += 2, kt += 2) {
@@ -197,25 +198,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g
     slab(kt + 1, a1, b1, a0, b0);
   }
   if (n & 1) slab(kt, a0, b0, a1, b1);
+  // the last MFMAs' accumulator writes before any other instruction reads them
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no copy may still be writing this workgroup's LDS
 
   // Epilogue through LDS, four rounds: in round i every wave stages its rows wm*128 + i*32 +
   // 0..31 as fp32 (stage pair i&1, the wm half in its own array, 16-byte chunks XOR-permuted
   // by row), then all threads store 64 full rows: bf16 outputs with 16-byte writes, or, for a
-  // split-K chunk, its fp32 partial tile (row-major 256 x 256) with 32-byte writes.  Lane
-  // (lr, lg) of MFMA tile (i, j) holds row lr and columns j*32 + 8*(r/4) + 4*lg + r%4.
+  // split-K chunk, its fp32 partial tile (row-major 256 x 256) with 32-byte writes.  Lane l of
+  // MFMA tile (i, j) holds row 16 i + l % 16 and columns 16 j + 4 (l / 16) + 0..3.
   float* part = tl >= 0 ? sk.partials + int64_t(tl * sk.split + chunk) * (BM * BN) : nullptr;
   lds_barrier();  // every wave is past its last fragment read
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < 4; ++i) {
     float* mine = reinterpret_cast<float*>((i & 1) ? (wm ? b1 : a1) : (wm ? b0 : a0));
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int c = wn * 32 + j * 8 + r4 * 2 + lg;
-        const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
-        *reinterpret_cast<f32x4*>(mine + lr * 256 + ((c ^ (lr & 15)) << 2)) = v;
+      for (int j = 0; j < NJ; ++j) {
+        const int row = 16 * h + lr, c = wn * 32 + 4 * j + lq;  // c: 16-byte chunk of the 256 columns
+        *reinterpret_cast<f32x4*>(mine + row * 256 + ((c ^ lr) << 2)) = acc[2 * i + h][j];
       }
     lds_barrier();
 #pragma unroll
