@@ -45,7 +45,12 @@ COLD_SCRUB_MIB = 512       # written between cold-cache steps (more than the 256
 # runs, scaled by the same counters read on a plain copy of known size.  Bytes
 # per launch; None until measured for the current kernel build.
 MEASURED_TRAFFIC_BYTES = {
-    # none yet for the 16x16x32 GEMM build (evenly spread slab copies)
+    # gemm_in main kernel + its split-K tail reduce (profiles/shard175b_kernels.md); set only for
+    # the GEMM build the counters were taken on (4-wave 128x128 as 16x16x32 MFMA tiles, 64-deep
+    # slabs, copies spread evenly over three phases, row-major split-K partials, epilogue with the
+    # variant steps and the 5-term erfc GeLU; tile-height and row-chunk publication template
+    # parameters, off for this launch)
+    "shard175b": 1026100374,
 }
 
 WORKLOAD_NOTES = {
