@@ -328,10 +328,10 @@ def test_deterministic_and_reusable_handle():
 
 
 def test_split_k_tails_on_a_reused_handle():
-    """Both GEMMs run entirely as split-K tail tiles at this shape (GEMM-in 8 x 21 = 168 tiles,
-    GEMM-out 8 x 4 = 32, fewer than one wave of 256), through the handle's partial-tile scratch:
-    20 forwards on one handle, every one bit-identical to the first, the first within tolerance
-    of the oracle."""
+    """The output GEMM runs entirely as split-K tail tiles at this shape (8 x 4 = 32 tiles on 256
+    compute units: 8 k-chunks each, no whole wave first), through the handle's partial-tile
+    scratch: 20 forwards on one handle, every one bit-identical to the first, the first within
+    tolerance of the oracle."""
     cfg = BlockConfig("tails", B=2, S=1024, d=1024, H=8, hd=128, ffn=2304, W=128, dtype="bf16")
     inp = make_inputs(cfg, seed=15, affine=True)
     dev = upload(inp)
@@ -351,6 +351,41 @@ def test_split_k_tails_on_a_reused_handle():
                                eps=cfg.ln_eps, add_residual=True)
     err = rel_err(from_dev(first).reshape(cfg.B, cfg.S, cfg.d), ref)
     log(f"[parity] split-K tails, reused handle: {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+# Shapes whose GEMMs end in a split-K tail after whole waves, on 256 compute units:
+#   "in_split4": GEMM-in 8 x 39 = 312 tiles = one wave + 56 tiles in 4 k-chunks; GEMM-out 8
+#     tiles in 32 k-chunks.
+#   "in_split3_out_split2": GEMM-in 16 x 21 = 336 tiles = one wave + 80 tiles in 3 k-chunks (the
+#     175B-shard GEMM-in's split); GEMM-out 16 x 24 = 384 tiles = one wave + 128 (2 k-chunks, or
+#     256 half-height tiles).
+SPLIT_TAILS = [
+    ("in_split4", 1, 2048, 256, 2, 128, 9216, 128),
+    ("in_split3_out_split2", 2, 2048, 6144, 4, 128, 3840, 256),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_TAILS, ids=[c[0] for c in SPLIT_TAILS])
+def test_split_k_tails_after_whole_waves(case):
+    """Every output of a forward whose GEMMs finish in a split-K tail wave after a whole one
+    (partials summed in chunk order by the reduce kernel) against the oracle, and three forwards
+    on one handle bit-identical."""
+    name, B, S, d, H, hd, ffn, W = case
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the tile counts above assume 256 compute units")
+    cfg = BlockConfig(name, B=B, S=S, d=d, H=H, hd=hd, ffn=ffn, W=W, dtype="bf16")
+    inp = make_inputs(cfg, seed=31, affine=True)
+    dev = upload(inp)
+    h = tb.pblock_create(cfg)
+    try:
+        y = run_block(cfg, dev, handle=h)
+        for _ in range(2):
+            assert np.array_equal(run_block(cfg, dev, handle=h), y)
+    finally:
+        tb.pblock_destroy(h)
+    err = rel_err(y.reshape(B, S, d), oracle_y(inp))
+    log(f"[parity] split-K tail {name}: {err:.3e}")
     assert err <= TOL["bf16"]
 
 
