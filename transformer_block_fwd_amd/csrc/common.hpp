@@ -32,9 +32,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(u >> 16);
 }
 
-// Two fp32 -> packed bf16 pair (lo in bits 0..15).
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even: one conversion
+// instruction for the pair (the same bits as f32_to_bf16 on each, for finite inputs).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const f32x2 pr = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -204,13 +204,15 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // Workgroup barrier that no memory access may be moved across (the waits are explicit).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Epilogue of 8 consecutive columns n .. n+7 of row m, one 16-byte store.
+// Epilogue of 8 consecutive columns n .. n+7 of row m, one 16-byte store.  Already loaded, when
+// not null: xres, the residual's 8 values (kEpiResidual); bpre, the bias of the 8 columns.
 template <int EPI>
-__device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f32x4 lo, f32x4 hi) {
+__device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f32x4 lo, f32x4 hi,
+                                             const u32x4* xres = nullptr, const u32x4* bpre = nullptr) {
   float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   uint16_t* dst;
   if (g.bias != nullptr) {
-    const u32x4 br = *reinterpret_cast<const u32x4*>(g.bias + n);
+    const u32x4 br = bpre != nullptr ? *bpre : *reinterpret_cast<const u32x4*>(g.bias + n);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[2 * e] += __uint_as_float(br[e] << 16);
@@ -255,7 +257,7 @@ __device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f3
     return;
   } else {
     if (g.resid != nullptr) {
-      const u32x4 xr = *reinterpret_cast<const u32x4*>(g.resid + int64_t(m) * g.ldr + n);
+      const u32x4 xr = xres != nullptr ? *xres : *reinterpret_cast<const u32x4*>(g.resid + int64_t(m) * g.ldr + n);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[2 * e] += __uint_as_float(xr[e] << 16);
@@ -266,6 +268,78 @@ __device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f3
   }
   const u32x4 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
   *reinterpret_cast<u32x4*>(dst) = o;
+}
+
+// Epilogue of a 256-column tile through LDS, BM/64 rounds: in round i every wave stages its
+// rows wm*BM/2 + i*32 + 0..31 as fp32 (stage pair i&1 of the LDS arrays, the wm half in its own
+// array, 16-byte chunks XOR-permuted by row), then all threads store 64 full rows: bf16 outputs
+// with 16-byte writes, or, for a split-K chunk, its fp32 partial tile (row-major BM x 256) with
+// 32-byte writes.  Lane l of MFMA tile (i, j) holds row 16 i + l % 16 and columns
+// 16 j + 4 (l / 16) + 0..3; the caller has made sure no wave still reads the LDS arrays.
+//
+// The store loop stays rolled: unrolled, its copies of every variant's branches made the
+// epilogue longer than the instruction cache, and it ran at the speed of instruction fetch.
+// The residual form is the exception: its loads are all issued at the start, each thread's 8
+// rows per round for every round, so that their latency is paid once per tile (one load in
+// flight at a time costs a memory latency per row), and its store loop is unrolled so that
+// they stay in registers.
+template <int EPI, int BM, int MI, int NJ>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI][NJ], uint16_t* a0, uint16_t* b0,
+                                              uint16_t* a1, uint16_t* b1, float* part, int m0, int n0, int wm,
+                                              int wn) {
+  constexpr int BN = kGemmBN, R = BM / 64;
+  constexpr bool kRes = EPI == kEpiResidual;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int c0 = (tid & 31) * 2, nl = (tid & 31) * 8;
+  // every row a thread stores has the same 8 columns: their bias is loaded once
+  u32x4 bias8 = {0u, 0u, 0u, 0u};
+  if (g.bias != nullptr && part == nullptr && n0 + nl < g.N) bias8 = *reinterpret_cast<const u32x4*>(g.bias + n0 + nl);
+  u32x4 xr[kRes ? R : 1][8];
+  if constexpr (kRes) {
+    if (part == nullptr && g.resid != nullptr) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int r = p * 8 + (tid >> 5);
+          const int ml = (r >> 5) * (BM / 2) + i * 32 + (r & 31);
+          if (m0 + ml < g.M && n0 + nl < g.N)
+            xr[i][p] = *reinterpret_cast<const u32x4*>(g.resid + int64_t(m0 + ml) * g.ldr + (n0 + nl));
+        }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float* mine = reinterpret_cast<float*>((i & 1) ? (wm ? b1 : a1) : (wm ? b0 : a0));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int row = 16 * h + lr, c = wn * 32 + 4 * j + lq;  // c: 16-byte chunk of the 256 columns
+        *reinterpret_cast<f32x4*>(mine + row * 256 + ((c ^ lr) << 2)) = acc[2 * i + h][j];
+      }
+    lds_barrier();
+#pragma unroll(kRes ? 8 : 1)
+    for (int p = 0; p < 8; ++p) {
+      const int r = p * 8 + (tid >> 5);
+      const int half = r >> 5, lrow = r & 31;
+      // a select between the LDS arrays themselves (through a pointer array the compiler loses
+      // the address space and reads LDS with flat loads)
+      const float* src = reinterpret_cast<const float*>((i & 1) ? (half ? b1 : a1) : (half ? b0 : a0));
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src + lrow * 256 + ((c0 ^ (lrow & 15)) << 2));
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + lrow * 256 + (((c0 + 1) ^ (lrow & 15)) << 2));
+      const int ml = half * (BM / 2) + i * 32 + lrow;
+      if (part != nullptr) {
+        f32x4* dst = reinterpret_cast<f32x4*>(part + ml * BN + nl);
+        dst[0] = lo;
+        dst[1] = hi;
+      } else if (m0 + ml < g.M && n0 + nl < g.N) {
+        if constexpr (kRes) store_chunk8<EPI>(g, m0 + ml, n0 + nl, lo, hi, g.resid != nullptr ? &xr[i][p] : nullptr, &bias8);
+        else store_chunk8<EPI>(g, m0 + ml, n0 + nl, lo, hi, nullptr, &bias8);
+      }
+    }
+  }
 }
 
 template <int EPI, int BM = kGemmBM, bool PUB = false>
@@ -470,42 +544,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no copy may still be writing this workgroup's LDS
 
-  // Epilogue through LDS, BM/64 rounds: in round i every wave stages its rows wm*BM/2 + i*32 +
-  // 0..31 as fp32 (stage pair i&1, the wm half in its own array, 16-byte chunks XOR-permuted
-  // by row), then all threads store 64 full rows: bf16 outputs with 16-byte writes, or, for a
-  // split-K chunk, its fp32 partial tile (row-major 256 x 256) with 32-byte writes.  Lane l of
-  // MFMA tile (i, j) holds row 16 i + l % 16 and columns 16 j + 4 (l / 16) + 0..3.
+  // Epilogue: split-K chunks store their fp32 partial tile, every other tile its outputs.
   float* part = tl >= 0 ? sk.partials + int64_t(tl * sk.split + chunk) * (BM * BN) : nullptr;
   lds_barrier();  // every wave is past its last fragment read
-#pragma unroll
-  for (int i = 0; i < BM / 64; ++i) {
-    float* mine = reinterpret_cast<float*>((i & 1) ? (wm ? b1 : a1) : (wm ? b0 : a0));
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int row = 16 * h + lr, c = wn * 32 + 4 * j + lq;  // c: 16-byte chunk of the 256 columns
-        *reinterpret_cast<f32x4*>(mine + row * 256 + ((c ^ lr) << 2)) = acc[2 * i + h][j];
-      }
-    lds_barrier();
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int r = p * 8 + (tid >> 5);
-      const int half = r >> 5, lrow = r & 31;
-      const float* src = reinterpret_cast<const float*>((i & 1) ? (half ? b1 : a1) : (half ? b0 : a0));
-      const int c0 = (tid & 31) * 2;
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(src + lrow * 256 + ((c0 ^ (lrow & 15)) << 2));
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + lrow * 256 + (((c0 + 1) ^ (lrow & 15)) << 2));
-      const int ml = half * (BM / 2) + i * 32 + lrow, nl = (tid & 31) * 8;
-      if (part != nullptr) {
-        f32x4* dst = reinterpret_cast<f32x4*>(part + ml * BN + nl);
-        dst[0] = lo;
-        dst[1] = hi;
-      } else if (m0 + ml < g.M && n0 + nl < g.N) {
-        store_chunk8<EPI>(g, m0 + ml, n0 + nl, lo, hi);
-      }
-    }
-  }
+  gemm_epilogue<EPI, BM>(g, acc, a0, b0, a1, b1, part, m0, n0, wm, wn);
   if constexpr (PUB) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // this thread's stores of the tile are done
     __syncthreads();

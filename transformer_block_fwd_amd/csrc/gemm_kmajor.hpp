@@ -204,42 +204,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no copy may still be writing this workgroup's LDS
 
-  // Epilogue through LDS, four rounds: in round i every wave stages its rows wm*128 + i*32 +
-  // 0..31 as fp32 (stage pair i&1, the wm half in its own array, 16-byte chunks XOR-permuted
-  // by row), then all threads store 64 full rows: bf16 outputs with 16-byte writes, or, for a
-  // split-K chunk, its fp32 partial tile (row-major 256 x 256) with 32-byte writes.  Lane l of
-  // MFMA tile (i, j) holds row 16 i + l % 16 and columns 16 j + 4 (l / 16) + 0..3.
+  // Epilogue: split-K chunks store their fp32 partial tile, every other tile its outputs.
   float* part = tl >= 0 ? sk.partials + int64_t(tl * sk.split + chunk) * (BM * BN) : nullptr;
   lds_barrier();  // every wave is past its last fragment read
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float* mine = reinterpret_cast<float*>((i & 1) ? (wm ? b1 : a1) : (wm ? b0 : a0));
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int row = 16 * h + lr, c = wn * 32 + 4 * j + lq;  // c: 16-byte chunk of the 256 columns
-        *reinterpret_cast<f32x4*>(mine + row * 256 + ((c ^ lr) << 2)) = acc[2 * i + h][j];
-      }
-    lds_barrier();
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int r = p * 8 + (tid >> 5);
-      const int half = r >> 5, lrow = r & 31;
-      const float* src = reinterpret_cast<const float*>((i & 1) ? (half ? b1 : a1) : (half ? b0 : a0));
-      const int c0 = (tid & 31) * 2;
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(src + lrow * 256 + ((c0 ^ (lrow & 15)) << 2));
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + lrow * 256 + (((c0 + 1) ^ (lrow & 15)) << 2));
-      const int ml = half * 128 + i * 32 + lrow, nl = (tid & 31) * 8;
-      if (part != nullptr) {
-        f32x4* dst = reinterpret_cast<f32x4*>(part + ml * BN + nl);
-        dst[0] = lo;
-        dst[1] = hi;
-      } else if (m0 + ml < g.M && n0 + nl < g.N) {
-        store_chunk8<EPI>(g, m0 + ml, n0 + nl, lo, hi);
-      }
-    }
-  }
+  gemm_epilogue<EPI, BM>(g, acc, a0, b0, a1, b1, part, m0, n0, wm, wn);
 }
 
 template <int EPI, bool AK>
