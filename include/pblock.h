@@ -346,7 +346,9 @@ int pblock_copy_intermediates(pblock_t h, void* u, void* qkv, void* ag, void* st
  * bwd_prep, bwd_gemm_dgrad, bwd_attention, bwd_gemm_wgrad, bwd_layernorm],
  * plus the number of timed calls (the serial form's two LayerNorms count as
  * layernorm, its QKV and FC1 GEMMs as gemm_in, its output-projection and FC2
- * GEMMs as gemm_out).  Enabling or disabling resets the sums.  n must be >= 4.
+ * GEMMs as gemm_out; in pblock_forward, when the input GEMM ends in a split-K
+ * tail of FC1 columns only, its reduce runs in the attention launch and counts
+ * as attention).  Enabling or disabling resets the sums.  n must be >= 4.
  * The events come from a pool of 256 calls per handle: when it is used up, the
  * next timed call first synchronises on the recorded events and folds them
  * into the sums, so with timing on, every 256th call waits for the earlier

@@ -85,8 +85,19 @@ __device__ __forceinline__ void attn_wait_copies() {
 }
 __device__ __forceinline__ void attn_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// LDS of one attention workgroup: K and V tiles of 64 rows in two stages.
 template <int HD>
-__global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs a) {
+struct AttnLds {
+  static constexpr int TB = kAttnBKV * HD * 2;
+  uint8_t k0[TB], v0[TB], k1[TB], v1[TB];
+};
+
+// One workgroup's (sequence, head, query tile) of the launch, blk in [0, B * H * tiles) (unsigned:
+// a signed division here cost the kernel 40 registers and spills), with
+// the calling kernel's own LDS (declared there: each kernel's LDS then sits at addresses known
+// when it is compiled, which the fragment reads fold into their offsets).
+template <int HD>
+__device__ __forceinline__ void swa_attn_block(const AttnArgs& a, unsigned blk, AttnLds<HD>& lds) {
   constexpr int BQ = kAttnBQ, BKV = kAttnBKV;
   constexpr int NW = kAttnThreads / 64;
   constexpr int ROWB = HD * 2;         // bytes per K/V row
@@ -96,16 +107,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
   constexpr int NH = HD / 32;          // 32-wide head-dim tiles of the output
   constexpr int NKK = HD / 16;         // 16-deep slices of the QK^T contraction
   static_assert(NIW * NW == NI, "copy instructions split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t k_st0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_st0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_st1[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_st1[TB];
+  uint8_t* const k_st0 = lds.k0;
+  uint8_t* const v_st0 = lds.v0;
+  uint8_t* const k_st1 = lds.k1;
+  uint8_t* const v_st1 = lds.v1;
 
   const int S = a.S, W = a.W;
   const int nqt = (a.q_hi - a.q_lo + BQ - 1) / BQ;
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int qt = nqt - 1 - blockIdx.x / BH;
+  const int bh = blk % BH;
+  const int qt = nqt - 1 - blk / BH;
   const int b = bh / a.H, h = bh % a.H;
   const int A = a.H * HD;
   const uint16_t* qbase = a.qkv + int64_t(b) * S * a.ld_qkv + h * HD;
@@ -318,6 +329,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs
         *reinterpret_cast<u32x2*>(orow + hd) = w;
       }
   }
+}
+
+template <int HD>
+__global__ __launch_bounds__(kAttnThreads, 2) void swa_attn_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) AttnLds<HD> lds;
+  swa_attn_block<HD>(a, blockIdx.x, lds);
 }
 
 }  // namespace pblk

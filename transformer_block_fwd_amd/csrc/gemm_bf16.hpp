@@ -183,7 +183,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 // Tile coordinates of linear tile index L: groups of kGroupM M-tiles, M fastest.
-__device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int* tm, int* tn) {
+__host__ __device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int* tm, int* tn) {
   const int group = kGroupM * tiles_n;
   const int first_m = (L / group) * kGroupM;
   const int gsz = min(tiles_m - first_m, kGroupM);
@@ -573,11 +573,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 // grid = tail * 32 workgroups of 256 threads; workgroup (tile, b) handles rows 8b .. 8b+7
 // of the tile, thread t row 8b + t/32 and columns 8*(t%32) .. +7: coalesced 32-byte
 // partial reads and 16-byte output writes.
+// Rows 8 blk .. 8 blk + 7 of the tail's tiles in order (32 row groups per tile).
 template <int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_tail_reduce_kernel(GemmArgs g, GemmSched sk) {
+__device__ __forceinline__ void tail_reduce_rows(const GemmArgs& g, const GemmSched& sk, int blk) {
   constexpr int BM = kGemmBM, BN = kGemmBN;
-  const int tl = blockIdx.x >> 5;
-  const int r = (blockIdx.x & 31) * 8 + (threadIdx.x >> 5);
+  const int tl = blk >> 5;
+  const int r = (blk & 31) * 8 + (threadIdx.x >> 5);
   const int c = (threadIdx.x & 31) * 8;
   int tm, tn;
   tile_coords(sk.dp_units + tl, sk.tiles_m, sk.tiles_n, &tm, &tn);
@@ -591,6 +592,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_tail_reduce_kernel(GemmArgs g, 
     hi += src[1];
   }
   store_chunk8<EPI>(g, m, n, lo, hi);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_tail_reduce_kernel(GemmArgs g, GemmSched sk) {
+  tail_reduce_rows<EPI>(g, sk, blockIdx.x);
 }
 
 }  // namespace pblk

@@ -26,6 +26,7 @@
 #include "attn_bf16.hpp"
 #include "attn_bwd_bf16.hpp"
 #include "attn_f32.hpp"
+#include "attn_tail.hpp"
 #include "backward.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
@@ -301,8 +302,15 @@ Split plan_split(int64_t T, int KT, int G) {
   return p;
 }
 
+// A split-K reduce left for the attention launch to run (see attn_tail.hpp).
+struct TailPending {
+  bool valid = false;
+  GemmArgs g;
+  GemmSched sk;
+};
+
 template <int EPI>
-void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s) {
+void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s, TailPending* defer = nullptr) {
   GemmSched sk;
   sk.partials = scr.partials;
   sk.wave_units = scr.G;
@@ -332,8 +340,24 @@ void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s) {
   sk.split = p.split;
   const unsigned grid = unsigned(p.dp_units + p.tail * p.split);
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk, RowPublish{});
-  if (p.tail > 0)
+  if (p.tail > 0) {
+    if (EPI == kEpiSplitGelu && defer != nullptr) {
+      // the reduce writes only FC1 columns when every tail tile starts at or past nsplit
+      bool fc1_only = true;
+      for (int tl = 0; tl < p.tail && fc1_only; ++tl) {
+        int tm, tn;
+        tile_coords(p.dp_units + tl, sk.tiles_m, sk.tiles_n, &tm, &tn);
+        fc1_only = tn * kGemmBN >= g.nsplit;
+      }
+      if (fc1_only) {
+        defer->valid = true;
+        defer->g = g;
+        defer->sk = sk;
+        return;
+      }
+    }
     hipLaunchKernelGGL((gemm_bf16_tail_reduce_kernel<EPI>), dim3(unsigned(p.tail * 32)), dim3(256), 0, s, g, sk);
+  }
 }
 
 // The output GEMM with row-chunk publication (pub.n, S, B, flags, counters, epoch set by the
@@ -388,7 +412,8 @@ void launch_gemm_f32(const GemmArgsF32& g, hipStream_t s) {
 
 // Attention for query positions [q_lo, q_hi) of each of the B sequences.
 void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, int B, int S, int H, int hd, int W,
-                      int dtype, hipStream_t s, int q_lo = 0, int q_hi = -1, float* lse = nullptr) {
+                      int dtype, hipStream_t s, int q_lo = 0, int q_hi = -1, float* lse = nullptr,
+                      const TailPending* tail = nullptr) {
   if (q_hi < 0) q_hi = S;
   // W >= S is full causal attention; clamping keeps every window sum in the kernels' int range
   W = std::min(W, S);
@@ -404,8 +429,22 @@ void launch_attention(const void* qkv, int64_t ld_qkv, void* o, int64_t ld_o, in
     a.q_lo = q_lo; a.q_hi = q_hi;
     a.scale_log2 = scale * 1.4426950408889634f;
     const unsigned grid = unsigned(((q_hi - q_lo + kAttnBQ - 1) / kAttnBQ) * int64_t(B) * H);
-    if (hd == 128) hipLaunchKernelGGL((swa_attn_bf16_kernel<128>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((swa_attn_bf16_kernel<64>), dim3(grid), dim3(256), 0, s, a);
+    if (tail != nullptr && tail->valid) {
+      // the input GEMM's split-K reduce in the same launch: 8 row groups (64 rows) per workgroup
+      constexpr int kRpw = 8;
+      const int n_groups = tail->sk.tail * 32;
+      const unsigned total = grid + unsigned((n_groups + kRpw - 1) / kRpw);
+      if (hd == 128)
+        hipLaunchKernelGGL((swa_attn_tail_kernel<128>), dim3(total), dim3(256), 0, s, a, int(grid), tail->g, tail->sk,
+                           kRpw, n_groups);
+      else
+        hipLaunchKernelGGL((swa_attn_tail_kernel<64>), dim3(total), dim3(256), 0, s, a, int(grid), tail->g, tail->sk,
+                           kRpw, n_groups);
+    } else if (hd == 128) {
+      hipLaunchKernelGGL((swa_attn_bf16_kernel<128>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((swa_attn_bf16_kernel<64>), dim3(grid), dim3(256), 0, s, a);
+    }
   } else {
     const dim3 grid{unsigned(int64_t((q_hi - q_lo + 63) / 64) * H * B)};
     const float* q = static_cast<const float*>(qkv);
@@ -581,7 +620,7 @@ struct InEpi {
 // Z = A B^T, A [M, K] (row stride lda), B [N, K] (row stride ldb).
 void run_gemm_in(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M, int64_t N, int64_t K, void* out0,
                  int64_t ld0, void* out1, int64_t ld1, int64_t off1, int64_t nsplit, int dtype, const SkScratch& scr,
-                 hipStream_t s, const InEpi& ep = InEpi{}) {
+                 hipStream_t s, const InEpi& ep = InEpi{}, TailPending* defer = nullptr) {
   if (dtype == PBLOCK_BF16) {
     GemmArgs g{};
     g.a = static_cast<const uint16_t*>(a); g.lda = lda;
@@ -595,7 +634,7 @@ void run_gemm_in(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t
     g.gelu_tanh = ep.gelu_tanh;
     g.pre = static_cast<uint16_t*>(ep.pre);
     g.ld_pre = ep.ld_pre;
-    launch_gemm_bf16<kEpiSplitGelu>(g, scr, s);
+    launch_gemm_bf16<kEpiSplitGelu>(g, scr, s, defer);
   } else {
     GemmArgsF32 g{};
     g.a = static_cast<const float*>(a); g.lda = lda;
@@ -752,10 +791,12 @@ void enqueue_forward(const Ws& ws, const void* x, const pblock_weights* w, const
   run_layernorm(x, w->ln_gamma, w->ln_beta, ws.u, dm.M, c, s);
   tm->mark(0);
   // Z = u W_in^T: Q|K|V columns to QKV, FC1 columns through GeLU to AG[:, A:]
+  // (a split-K reduce of FC1-only tail tiles runs inside the attention launch)
+  TailPending tail;
   run_gemm_in(ws.u, c.d, w->w_in, c.d, dm.M, dm.n_in, c.d, ws.qkv, 3 * A, ws.ag, dm.k_out, A, 3 * A, c.dtype, ws.scr,
-              s);
+              s, InEpi{}, &tail);
   tm->mark(1);
-  launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s);
+  launch_attention(ws.qkv, 3 * A, ws.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s, 0, -1, nullptr, &tail);
   tm->mark(2);
   // y = [attention | GeLU] W_out^T (+ x): both branches summed in one accumulator
   run_gemm_out(ws.ag, dm.k_out, w->w_out, dm.k_out, dm.M, c.d, dm.k_out, out, c.add_residual ? x : nullptr, c.dtype,
