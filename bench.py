@@ -12,15 +12,16 @@ events: `value`, `ms_per_step`), then the same K steps again with HIP events
 around every step and every kernel launch (`instrumented`: the per-step spread,
 the per-kernel times and the roofline record of the dominant kernel), then the
 other measurements.  From a cold start the forward needs about 30 steps to reach
-its sustained rate (`--ramp`), so with few warm-up steps the timed region
-includes part of that ramp.
+its sustained rate (`--ramp` records that ramp step by step); the default 40
+warm-up steps cover it, so `value` is the sustained rate (with fewer warm-up
+steps the timed region includes part of the ramp).
 
 Prints ONE JSON line: throughput in TFLOP/s of algorithmic work, % of the bf16
 MFMA peak, tokens/s, the instrumented pass, a cold-cache pass, per-kernel times,
 the roofline record, the MFMA-loop rate, and the fp64 CPU oracle timed on the
 host as a baseline.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload shard175b]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 40] [--workload shard175b]
                   [--block parallel|serial] [--window W] [--chunks N]
                   [--gelu-tanh] [--bias] [--rope BASE] [--two-ln]   # variant switches
                   [--train]    # forward with saved activations + backward pass
@@ -65,7 +66,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--block", choices=("parallel", "serial"), default="parallel",
                    help="the parallel block (default) or the serial pre-LN layer from the same kernels")
