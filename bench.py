@@ -46,12 +46,12 @@ COLD_SCRUB_MIB = 512       # written between cold-cache steps (more than the 256
 # runs, scaled by the same counters read on a plain copy of known size.  Bytes
 # per launch; None until measured for the current kernel build.
 MEASURED_TRAFFIC_BYTES = {
-    # gemm_in main kernel + its split-K tail reduce (profiles/shard175b_kernels.md); set only for
-    # the GEMM build the counters were taken on (4-wave 128x128 as 16x16x32 MFMA tiles, 64-deep
-    # slabs, copies spread evenly over three phases, row-major split-K partials, epilogue with the
-    # variant steps and the 5-term erfc GeLU; tile-height and row-chunk publication template
-    # parameters, off for this launch)
-    "shard175b": 1026100374,
+    # gemm_in main kernel (profiles/shard175b_kernels.md; its split-K reduce runs in the attention
+    # launch); set only for the GEMM build the counters were taken on (4-wave 128x128 as 16x16x32
+    # MFMA tiles, 64-deep slabs, copies spread evenly over three phases, row-major split-K
+    # partials, the epilogue's store loop rolled with the residual loaded ahead, the 5-term erfc
+    # GeLU; tile-height and row-chunk publication template parameters, off for this launch)
+    "shard175b": 953630613,
 }
 
 WORKLOAD_NOTES = {
