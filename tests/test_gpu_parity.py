@@ -360,9 +360,14 @@ def test_split_k_tails_on_a_reused_handle():
 #   "in_split3_out_split2": GEMM-in 16 x 21 = 336 tiles = one wave + 80 tiles in 3 k-chunks (the
 #     175B-shard GEMM-in's split); GEMM-out 16 x 24 = 384 tiles = one wave + 128 (2 k-chunks, or
 #     256 half-height tiles).
+#   "in_tail_holds_qkv": GEMM-in 8 x 37 = 296 tiles = one wave + 40 tiles in 4 k-chunks, the
+#     first of them Q, K, V columns (3A = 9216 > 8192): their reduce must run before attention
+#     (in the first two cases the tail is FC1 columns only and its reduce runs inside the
+#     attention launch).
 SPLIT_TAILS = [
     ("in_split4", 1, 2048, 256, 2, 128, 9216, 128),
     ("in_split3_out_split2", 2, 2048, 6144, 4, 128, 3840, 256),
+    ("in_tail_holds_qkv", 1, 2048, 256, 24, 128, 256, 128),
 ]
 
 
