@@ -45,7 +45,10 @@
 // When whole waves come first and the remainder would be cut in two k-chunks (between a
 // third and a half of a wave of tiles), it runs instead as twice as many 128 x 256
 // half-height tiles in a second launch of the BM = 128 form: one wave, every tile whole,
-// no partials.
+// no partials.  Before either: when 256 x 192 tiles (the BN = 192 form, each wavefront
+// 128 x 96 as 8 x 6 MFMA tiles) fill whole waves where 256 x 256 tiles leave a partial one,
+// the GEMM runs as those, every tile whole (the 175B shard's output GEMM: 8 x 64 = 512 tiles,
+// two waves, against 384 = 1.5 waves of 256 x 256).
 //
 // L2 locality: workgroup ids are remapped so each XCD (id mod 8) owns a
 // contiguous run of work units, and units are ordered in groups of 8 M-tiles
@@ -283,18 +286,20 @@ __device__ __forceinline__ void store_chunk8(const GemmArgs& g, int m, int n, f3
 // rows per round for every round, so that their latency is paid once per tile (one load in
 // flight at a time costs a memory latency per row), and its store loop is unrolled so that
 // they stay in registers.
-template <int EPI, int BM, int MI, int NJ>
+template <int EPI, int BM, int MI, int NJ, int BN = kGemmBN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI][NJ], uint16_t* a0, uint16_t* b0,
                                               uint16_t* a1, uint16_t* b1, float* part, int m0, int n0, int wm,
                                               int wn) {
-  constexpr int BN = kGemmBN, R = BM / 64;
+  constexpr int R = BM / 64;
   constexpr bool kRes = EPI == kEpiResidual;
+  static_assert(BN == 2 * 16 * NJ && BN <= 256, "two wavefronts of NJ 16-column blocks across the tile");
   const int tid = threadIdx.x, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
   const int c0 = (tid & 31) * 2, nl = (tid & 31) * 8;
+  const bool col_ok = nl < BN;  // a 192-column tile leaves the last 8 threads of each row idle
   // every row a thread stores has the same 8 columns: their bias is loaded once
   u32x4 bias8 = {0u, 0u, 0u, 0u};
-  if (g.bias != nullptr && part == nullptr && n0 + nl < g.N) bias8 = *reinterpret_cast<const u32x4*>(g.bias + n0 + nl);
+  if (g.bias != nullptr && part == nullptr && col_ok && n0 + nl < g.N) bias8 = *reinterpret_cast<const u32x4*>(g.bias + n0 + nl);
   u32x4 xr[kRes ? R : 1][8];
   if constexpr (kRes) {
     if (part == nullptr && g.resid != nullptr) {
@@ -304,7 +309,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI
         for (int p = 0; p < 8; ++p) {
           const int r = p * 8 + (tid >> 5);
           const int ml = (r >> 5) * (BM / 2) + i * 32 + (r & 31);
-          if (m0 + ml < g.M && n0 + nl < g.N)
+          if (col_ok && m0 + ml < g.M && n0 + nl < g.N)
             xr[i][p] = *reinterpret_cast<const u32x4*>(g.resid + int64_t(m0 + ml) * g.ldr + (n0 + nl));
         }
     }
@@ -316,7 +321,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int row = 16 * h + lr, c = wn * 32 + 4 * j + lq;  // c: 16-byte chunk of the 256 columns
+        const int row = 16 * h + lr, c = wn * (BN / 8) + 4 * j + lq;  // c: 16-byte chunk of the row
         *reinterpret_cast<f32x4*>(mine + row * 256 + ((c ^ lr) << 2)) = acc[2 * i + h][j];
       }
     lds_barrier();
@@ -330,7 +335,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI
       const f32x4 lo = *reinterpret_cast<const f32x4*>(src + lrow * 256 + ((c0 ^ (lrow & 15)) << 2));
       const f32x4 hi = *reinterpret_cast<const f32x4*>(src + lrow * 256 + (((c0 + 1) ^ (lrow & 15)) << 2));
       const int ml = half * (BM / 2) + i * 32 + lrow;
-      if (part != nullptr) {
+      if (!col_ok) {
+      } else if (part != nullptr) {
         f32x4* dst = reinterpret_cast<f32x4*>(part + ml * BN + nl);
         dst[0] = lo;
         dst[1] = hi;
@@ -342,15 +348,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI
   }
 }
 
-template <int EPI, int BM = kGemmBM, bool PUB = false>
+template <int EPI, int BM = kGemmBM, bool PUB = false, int BN = kGemmBN>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, GemmSched sk, RowPublish pub) {
   static_assert(BM == 256 || BM == 128, "tile height 256 or 128");
-  constexpr int BN = kGemmBN, BK = kGemmBK, NT = kGemmThreads;
-  constexpr int MI = BM / 32, NJ = 8;  // 16x16 MFMA tiles per wavefront (BM/2 x 128)
+  static_assert(BN == 256 || (BN == 192 && BM == 256 && !PUB), "tile width 256, or 192 for whole waves");
+  constexpr int BK = kGemmBK, NT = kGemmThreads;
+  constexpr int MI = BM / 32, NJ = BN / 32;  // 16x16 MFMA tiles per wavefront (BM/2 x BN/2)
   constexpr int P = MI * NJ / 2;       // MFMAs per phase (half a 32-deep k-step)
   constexpr int NR = MI + NJ;          // fragment reads per k-step
-  constexpr int NA = BM / 32;          // A copy instructions per wavefront and slab (B: 8)
-  constexpr int NC = NA + 8;           // copy instructions per wavefront and slab
+  constexpr int NA = BM / 32;          // A copy instructions per wavefront and slab
+  constexpr int NB = BN / 32;          // B copy instructions per wavefront and slab
+  constexpr int NC = NA + NB;          // copy instructions per wavefront and slab
   constexpr int C12 = (2 * NC + 2) / 3;  // of them issued in phases 2 and 3 (see copy_pos)
   __shared__ __attribute__((aligned(1024))) uint16_t a0[kGemmHalf];
   __shared__ __attribute__((aligned(1024))) uint16_t b0[kGemmHalf];
@@ -395,9 +403,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   }
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // Copies: instruction i (0..7) of wave w fills 1 KiB block 8w + i of each operand tile =
-  // rows 64w + 8i + l/8; lane l writes physical chunk l%8, fetched from logical chunk
-  // (l%8) ^ ((row >> 1) & 7) = (l%8) ^ (4*(i&1) + l/16).
+  // Copies: B instruction i (0 .. NB-1) of wave w fills 1 KiB block NB w + i of the B tile =
+  // rows (BN/4) w + 8i + l/8; lane l writes physical chunk l%8, fetched from logical chunk
+  // (l%8) ^ ((row >> 1) & 7) = (l%8) ^ (4*(i&1) + l/16) (BN/4 is a multiple of 16).
   const uint32_t lda_b = uint32_t(g.lda) * 2u, ldb_b = uint32_t(g.ldb) * 2u;
   uint32_t offa[2], offb[2];
 #pragma unroll
@@ -409,7 +417,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   // A: wave w's NA instructions fill rows w*BM/4 .. +BM/4 (1 KiB block w*NA + i = rows
   // w*BM/4 + 8i + l/8: the same row swizzle, since BM/4 is a multiple of 16)
   const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(g.a) + int64_t(m0 + wave * (BM / 4)) * lda_b;
-  // copy instruction i of slab kt: A (i < NA) and B (i < 8)
+  // copy instruction i of slab kt: A (i < NA) and B (i < NB)
   auto issue_a = [&](int kt, uint16_t* sa, int i) __attribute__((always_inline)) {
     const uint32_t kofs = uint32_t(kt) * (BK * 2);
     __builtin_amdgcn_global_load_lds(a_blk + int64_t(8 * i) * lda_b + kofs + offa[i & 1],
@@ -417,24 +425,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   };
   auto issue_b = [&](int kt, uint16_t* sb, int i) __attribute__((always_inline)) {
     const uint32_t kofs = uint32_t(kt) * (BK * 2);
-    const int brow = min(n0 + wave * 64 + 8 * i, g.N - 8);
+    const int brow = min(n0 + wave * (BN / 4) + 8 * i, g.N - 8);
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(g.b) + int64_t(brow) * ldb_b + kofs + offb[i & 1],
-                                     (PBLK_LDS void*)(sb + (wave * 8 + i) * 512), 16, 0, 0);
+                                     (PBLK_LDS void*)(sb + (wave * NB + i) * 512), 16, 0, 0);
   };
   // copy instructions i0 .. i1-1 of slab kt
   auto issue = [&](int kt, uint16_t* sa, uint16_t* sb, int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
       if (i < NA) issue_a(kt, sa, i);
-      issue_b(kt, sb, i);
+      if (i < NB) issue_b(kt, sb, i);
     }
   };
-  // Copy c (0 .. NC-1) of a slab: the A and B instructions of i = c / 2 alternately while
-  // i < NA, then the remaining B instructions.
+  // Copy c (0 .. NC-1) of a slab: the A and B instructions of i = c / 2 alternately while both
+  // have one, then the remaining instructions of the other operand.
+  constexpr int NMIN = NA < NB ? NA : NB;
   auto copy1 = [&](int kt, uint16_t* sa, uint16_t* sb, int c) __attribute__((always_inline)) {
-    if (c < 2 * NA) {
+    if (c < 2 * NMIN) {
       if (c & 1) issue_b(kt, sb, c >> 1);
       else issue_a(kt, sa, c >> 1);
+    } else if (NA > NB) {
+      issue_a(kt, sa, c - NB);
     } else {
       issue_b(kt, sb, c - NA);
     }
@@ -449,7 +460,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   for (int ks = 0; ks < 2; ++ks) {
     const uint32_t o = uint32_t(lr * 128 + (((4 * ks + lq) ^ ((lr >> 1) & 7)) << 4));
     rda[ks] = o + uint32_t(wm * (BM / 2) * 128);
-    rdb[ks] = o + uint32_t(wn * 128 * 128);
+    rdb[ks] = o + uint32_t(wn * (BN / 2) * 128);
   }
 
   f32x4 acc[MI][NJ];
@@ -521,9 +532,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
     phase(1, 1, NR, 0, na, nb, 0, 3, tc, wa, wb);
   };
 
-  issue(kb, a0, b0, 0, 8);
-  issue(min(kb + 1, ke - 1), a1, b1, 0, 8);
-  wait_vm_lgkm0<NA + 8>();  // slab kb landed
+  constexpr int NMAX = NA > NB ? NA : NB;
+  issue(kb, a0, b0, 0, NMAX);
+  issue(min(kb + 1, ke - 1), a1, b1, 0, NMAX);
+  wait_vm_lgkm0<NC>();  // slab kb landed
   lds_barrier();
 #pragma unroll
   for (int x = 0; x < NR; ++x) rd1(0, a0, b0, 0, x);
@@ -547,7 +559,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
   // Epilogue: split-K chunks store their fp32 partial tile, every other tile its outputs.
   float* part = tl >= 0 ? sk.partials + int64_t(tl * sk.split + chunk) * (BM * BN) : nullptr;
   lds_barrier();  // every wave is past its last fragment read
-  gemm_epilogue<EPI, BM>(g, acc, a0, b0, a1, b1, part, m0, n0, wm, wn);
+  gemm_epilogue<EPI, BM, MI, NJ, BN>(g, acc, a0, b0, a1, b1, part, m0, n0, wm, wn);
   if constexpr (PUB) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // this thread's stores of the tile are done
     __syncthreads();
