@@ -354,28 +354,38 @@ def test_split_k_tails_on_a_reused_handle():
     assert err <= TOL["bf16"]
 
 
-# Shapes whose GEMMs end in a split-K tail after whole waves, on 256 compute units:
+# Shapes whose GEMMs would end in a partial wave of 256 x 256 tiles, on 256 compute units:
 #   "in_split4": GEMM-in 8 x 39 = 312 tiles = one wave + 56 tiles in 4 k-chunks; GEMM-out 8
 #     tiles in 32 k-chunks.
-#   "in_split3_out_split2": GEMM-in 16 x 21 = 336 tiles = one wave + 80 tiles in 3 k-chunks (the
-#     175B-shard GEMM-in's split); GEMM-out 16 x 24 = 384 tiles = one wave + 128 (2 k-chunks, or
-#     256 half-height tiles).
+#   "in_split3_out_wide": GEMM-in 16 x 21 = 336 tiles = one wave + 80 tiles in 3 k-chunks (the
+#     175B-shard GEMM-in's split); GEMM-out 16 x 24 = 384 tiles of 256 x 256, run as one wave of
+#     16 x 16 tiles of 256 x 384.
 #   "in_tail_holds_qkv": GEMM-in 8 x 37 = 296 tiles = one wave + 40 tiles in 4 k-chunks, the
 #     first of them Q, K, V columns (3A = 9216 > 8192): their reduce must run before attention
 #     (in the first two cases the tail is FC1 columns only and its reduce runs inside the
 #     attention launch).
+#   "out_wide_odd_k": GEMM-out 4096 x 6144 with k = 320, an odd number of 64-deep slabs, in
+#     256 x 384 tiles.
+#   "out_192": GEMM-out 16 x 36 = 576 tiles of 256 x 256; 256 x 384 tiles would be 384 (a wave
+#     and a half), 256 x 192 tiles are 768 = three whole waves: those.
+#   "out_half_height": GEMM-out 16 x 23 = 368 tiles = one wave + 112, which neither 384- nor
+#     192-wide tiles turn into whole waves: the 112 run as 224 tiles of 128 x 256.
 SPLIT_TAILS = [
     ("in_split4", 1, 2048, 256, 2, 128, 9216, 128),
-    ("in_split3_out_split2", 2, 2048, 6144, 4, 128, 3840, 256),
+    ("in_split3_out_wide", 2, 2048, 6144, 4, 128, 3840, 256),
     ("in_tail_holds_qkv", 1, 2048, 256, 24, 128, 256, 128),
+    ("out_wide_odd_k", 2, 2048, 6144, 1, 128, 192, 64),
+    ("out_192", 2, 2048, 9216, 2, 128, 256, 128),
+    ("out_half_height", 2, 2048, 5888, 2, 128, 256, 128),
 ]
 
 
 @pytest.mark.parametrize("case", SPLIT_TAILS, ids=[c[0] for c in SPLIT_TAILS])
 def test_split_k_tails_after_whole_waves(case):
-    """Every output of a forward whose GEMMs finish in a split-K tail wave after a whole one
-    (partials summed in chunk order by the reduce kernel) against the oracle, and three forwards
-    on one handle bit-identical."""
+    """Every output of a forward whose GEMMs would leave a partial wave of 256 x 256 tiles (a
+    split-K tail summed in chunk order by the reduce kernel, 384- or 192-wide tiles in whole
+    waves, or half-height tiles) against the oracle, and three forwards on one handle
+    bit-identical."""
     name, B, S, d, H, hd, ffn, W = case
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the tile counts above assume 256 compute units")

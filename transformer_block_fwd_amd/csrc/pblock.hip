@@ -31,6 +31,7 @@
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
 #include "gemm_kmajor.hpp"
+#include "gemm_wide.hpp"
 #include "layernorm.hpp"
 #include "rowchunks.hpp"
 
@@ -319,6 +320,19 @@ void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s, Ta
   sk.KT = g.K / kGemmBK;
   sk.unit_base = 0;
   const Split p = plan_split(int64_t(sk.tiles_m) * sk.tiles_n, sk.KT, scr.G);
+  if constexpr (EPI == kEpiResidual) {
+    const int tiles_nw = g.N / kWideBN;
+    if (p.tail > 0 && g.N % kWideBN == 0 && int64_t(sk.tiles_m) * tiles_nw % scr.G == 0) {
+      // 256 x 256 tiles leave a partial wave, 256 x 384 tiles fill whole waves: those, every
+      // tile whole (3/2 of the work per tile at 5/4 of the operand traffic)
+      sk.tiles_n = tiles_nw;
+      sk.dp_units = sk.tiles_m * tiles_nw;
+      sk.tail = 0;
+      sk.split = 1;
+      hipLaunchKernelGGL((gemm_bf16_wide_kernel<EPI>), dim3(unsigned(sk.dp_units)), dim3(kGemmThreads), 0, s, g, sk);
+      return;
+    }
+  }
   const int tiles_n192 = (g.N + 191) / 192;
   if (p.tail > 0 && int64_t(sk.tiles_m) * tiles_n192 % scr.G == 0) {
     // 256 x 256 tiles leave a partial wave, 256 x 192 tiles fill whole waves: those, every tile
