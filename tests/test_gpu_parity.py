@@ -359,7 +359,7 @@ def test_split_k_tails_on_a_reused_handle():
 #     tiles in 32 k-chunks.
 #   "in_split3_out_wide": GEMM-in 16 x 21 = 336 tiles = one wave + 80 tiles in 3 k-chunks (the
 #     175B-shard GEMM-in's split); GEMM-out 16 x 24 = 384 tiles of 256 x 256, run as one wave of
-#     16 x 16 tiles of 256 x 384.
+#     16 x 16 tiles of 256 x 384 (k = 4288, an odd number of 64-deep slabs).
 #   "in_tail_holds_qkv": GEMM-in 8 x 37 = 296 tiles = one wave + 40 tiles in 4 k-chunks, the
 #     first of them Q, K, V columns (3A = 9216 > 8192): their reduce must run before attention
 #     (in the first two cases the tail is FC1 columns only and its reduce runs inside the
@@ -372,7 +372,7 @@ def test_split_k_tails_on_a_reused_handle():
 #     192-wide tiles turn into whole waves: the 112 run as 224 tiles of 128 x 256.
 SPLIT_TAILS = [
     ("in_split4", 1, 2048, 256, 2, 128, 9216, 128),
-    ("in_split3_out_wide", 2, 2048, 6144, 4, 128, 3840, 256),
+    ("in_split3_out_wide", 2, 2048, 6144, 4, 128, 3776, 256),
     ("in_tail_holds_qkv", 1, 2048, 256, 24, 128, 256, 128),
     ("out_wide_odd_k", 2, 2048, 6144, 1, 128, 192, 64),
     ("out_192", 2, 2048, 9216, 2, 128, 256, 128),
