@@ -56,9 +56,14 @@
 // block of tiles at the same k, so they share activation and weight slabs in
 // that XCD's L2.
 //
-// Epilogue: the accumulators go out through LDS in four rounds of 64 rows
-// (fp32, chunk-permuted), so every global store is a full 16-byte piece of a
-// row and a wavefront writes whole 512-byte rows.
+// Epilogue, two forms chosen by the host (template parameter DIRECT):
+//   direct, for launches with no bias, rotary step, saved pre-activation, tanh GeLU or residual
+//     (the plain forward) and their split-K partials: one v_permlane16_swap per accumulator
+//     register pairs up two 16-column MFMA blocks so that every lane holds 8 consecutive
+//     columns of one row, stored with one 16-byte write (no LDS, no barriers);
+//   staged, for the rest: the accumulators go out through LDS in four rounds of 64 rows
+//     (fp32, chunk-permuted), so every global store is a full 16-byte piece of a row and a
+//     wavefront writes whole 512-byte rows.
 //   kEpiSplitGelu: columns < nsplit are stored as bf16 to out0 (the Q|K|V
 //     projections); columns >= nsplit get the exact GeLU and go to out1 at
 //     column off1 + (n - nsplit) (the FC1 activations next to the attention
@@ -348,10 +353,72 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI
   }
 }
 
-template <int EPI, int BM = kGemmBM, bool PUB = false, int BN = kGemmBN>
+// 8 consecutive columns n .. n+7 of row m for the direct epilogue's forms: Q|K|V columns stored
+// as they are, FC1 columns through the exact GeLU, or the output GEMM's plain rounding.
+template <int EPI>
+__device__ __forceinline__ void store_plain8(const GemmArgs& g, int m, int n, const f32x4& lo, const f32x4& hi) {
+  float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  uint16_t* dst;
+  if constexpr (EPI == kEpiSplitGelu) {
+    if (n < g.nsplit) {
+      dst = g.out0 + int64_t(m) * g.ld0 + n;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = gelu_erf_bf16out(v[e]);
+      dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
+    }
+  } else {
+    dst = g.out0 + int64_t(m) * g.ld0 + n;
+  }
+  const u32x4 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  *reinterpret_cast<u32x4*>(dst) = o;
+}
+
+// Epilogue without LDS staging, for launches with no bias, rotary step, saved pre-activation,
+// tanh GeLU or residual (the host picks the kernel form: with both epilogues in one kernel the
+// register allocator spills accumulators), and their split-K partials.
+// For every 16-row block i and pair of 16-column blocks (2 jp, 2 jp + 1), one v_permlane16_swap
+// per accumulator register exchanges 16-lane rows between the two blocks' accumulators: lane l
+// of block j holds row l % 16, columns 4 (l / 16) + 0..3; after the swap the first register set
+// holds columns 0..3 and the second 4..7 of one 8-column chunk, block 2 jp for lanes 0-15 and
+// 32-47 (chunk columns 0 and 8), block 2 jp + 1 for lanes 16-31 and 48-63 (columns 16 and 24 of
+// the pair).  Each lane then stores one 16-byte piece (a wave writes 64 contiguous bytes of each
+// of 16 rows), or for a split-K chunk its fp32 partial (row-major BM x BN, 32-byte writes).
+template <int EPI, int BM, int MI, int NJ, int BN>
+__device__ __forceinline__ void gemm_epilogue_direct(const GemmArgs& g, f32x4 (&acc)[MI][NJ], float* part, int m0,
+                                                     int n0, int wm, int wn) {
+  static_assert(NJ % 2 == 0, "pairs of 16-column blocks");
+  const int lane = threadIdx.x & 63;
+  const int mrow = wm * (BM / 2) + (lane & 15);
+  const int ncol = wn * (BN / 2) + 16 * ((lane >> 4) & 1) + 8 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int jp = 0; jp < NJ / 2; ++jp) {
+      f32x4 lo, hi;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][2 * jp][k]),
+                                                        __float_as_uint(acc[i][2 * jp + 1][k]), false, false);
+        lo[k] = __uint_as_float(r[0]);
+        hi[k] = __uint_as_float(r[1]);
+      }
+      const int ml = mrow + 16 * i, nl = ncol + 32 * jp;
+      if (part != nullptr) {
+        f32x4* dst = reinterpret_cast<f32x4*>(part + ml * BN + nl);
+        dst[0] = lo;
+        dst[1] = hi;
+      } else if (m0 + ml < g.M && n0 + nl < g.N) {
+        store_plain8<EPI>(g, m0 + ml, n0 + nl, lo, hi);
+      }
+    }
+}
+
+template <int EPI, int BM = kGemmBM, bool PUB = false, int BN = kGemmBN, bool DIRECT = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, GemmSched sk, RowPublish pub) {
   static_assert(BM == 256 || BM == 128, "tile height 256 or 128");
   static_assert(BN == 256 || (BN == 192 && BM == 256 && !PUB), "tile width 256, or 192 for whole waves");
+  static_assert(!DIRECT || ((EPI == kEpiSplitGelu || EPI == kEpiResidual) && !PUB), "direct epilogue forms");
   constexpr int BK = kGemmBK, NT = kGemmThreads;
   constexpr int MI = BM / 32, NJ = BN / 32;  // 16x16 MFMA tiles per wavefront (BM/2 x BN/2)
   constexpr int P = MI * NJ / 2;       // MFMAs per phase (half a 32-deep k-step)
@@ -558,8 +625,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, 
 
   // Epilogue: split-K chunks store their fp32 partial tile, every other tile its outputs.
   float* part = tl >= 0 ? sk.partials + int64_t(tl * sk.split + chunk) * (BM * BN) : nullptr;
-  lds_barrier();  // every wave is past its last fragment read
-  gemm_epilogue<EPI, BM, MI, NJ, BN>(g, acc, a0, b0, a1, b1, part, m0, n0, wm, wn);
+  if constexpr (DIRECT) {
+    gemm_epilogue_direct<EPI, BM, MI, NJ, BN>(g, acc, part, m0, n0, wm, wn);
+  } else {
+    lds_barrier();  // every wave is past its last fragment read
+    gemm_epilogue<EPI, BM, MI, NJ, BN>(g, acc, a0, b0, a1, b1, part, m0, n0, wm, wn);
+  }
   if constexpr (PUB) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // this thread's stores of the tile are done
     __syncthreads();

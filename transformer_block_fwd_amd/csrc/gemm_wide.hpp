@@ -28,12 +28,15 @@
 //   1, 6, .., 81 of the next slab: one every 5 MFMAs, so that a CU's copy path (about 64 bytes
 //   per clock) never takes a burst, and the last one lands about 95 MFMAs before it is needed.
 //
-// The epilogue stages the accumulators through LDS in 8 rounds of 16 rows per wavefront row
-// (fp32, 16-byte chunks XOR-permuted by row); every thread then stores 6 chunks of 8 columns
-// with 16-byte writes, consecutive threads on consecutive chunks of a row.
+// Epilogue: the lane-swap one of gemm_bf16_kernel (no LDS) in the DIRECT form, which the host
+// launches when there is no bias or residual (the 175B shard's partial output); otherwise the
+// accumulators go through LDS in 8 rounds of 16 rows per wavefront row (fp32, 16-byte chunks
+// XOR-permuted by row), and every thread stores 6 chunks of 8 columns with 16-byte writes,
+// consecutive threads on consecutive chunks of a row.
 //
 // Requirements (checked by the launcher): N % 384 == 0, K % 64 == 0, A allocated in whole
-// 256-row tiles, every tile whole (no k-split), EPI kEpiResidual.
+// 256-row tiles, every tile whole (no k-split), EPI kEpiResidual; the DIRECT form only without
+// bias or residual.
 #pragma once
 
 #include "gemm_bf16.hpp"
@@ -42,7 +45,7 @@ namespace pblk {
 
 constexpr int kWideBN = 384;
 
-template <int EPI>
+template <int EPI, bool DIRECT = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_wide_kernel(GemmArgs g, GemmSched sk) {
   constexpr int BM = kGemmBM, BN = kWideBN, BK = kGemmBK;
   constexpr int MI = 8, NJ = 12, NJA = 8;  // per wavefront 128 x 192; column blocks < NJA in AGPRs
@@ -198,31 +201,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_wide_kernel(GemmArg
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no copy may still be writing this workgroup's LDS
-  lds_barrier();                       // every wave is past its last fragment read
+  if constexpr (DIRECT) {
+    // no bias or residual: the lane-swap epilogue of gemm_bf16_kernel, no LDS
+    gemm_epilogue_direct<EPI, BM, MI, NJ, BN>(g, acc, nullptr, m0, n0, wm, wn);
+  } else {
+    lds_barrier();  // every wave is past its last fragment read
 
-  // Epilogue: round r stages MFMA row block r of every wavefront (rows 128 wm + 16 r + 0..15,
-  // the wavefront's 192 columns) as fp32 into buffer pair r & 1 (a0 / a1 for even rounds, b0 / b1
-  // for odd ones, the wm half in its own array; 16 rows x 384 columns = 24 KiB each), then the
-  // 256 threads store the round's 32 rows x 48 chunks of 8 columns.
+    // Epilogue: round r stages MFMA row block r of every wavefront (rows 128 wm + 16 r + 0..15,
+    // the wavefront's 192 columns) as fp32 into buffer pair r & 1 (a0 / a1 for even rounds, b0 / b1
+    // for odd ones, the wm half in its own array; 16 rows x 384 columns = 24 KiB each), then the
+    // 256 threads store the round's 32 rows x 48 chunks of 8 columns.
 #pragma unroll
-  for (int r = 0; r < MI; ++r) {
-    float* mine = reinterpret_cast<float*>((r & 1) ? (wm ? b1 : b0) : (wm ? a1 : a0));
+    for (int r = 0; r < MI; ++r) {
+      float* mine = reinterpret_cast<float*>((r & 1) ? (wm ? b1 : b0) : (wm ? a1 : a0));
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = wn * (BN / 8) + 4 * j + lq;  // 16-byte chunk of the row (0..95)
-      *reinterpret_cast<f32x4*>(mine + lr * BN + ((c ^ lr) << 2)) = acc[r][j];
-    }
-    lds_barrier();
+      for (int j = 0; j < NJ; ++j) {
+        const int c = wn * (BN / 8) + 4 * j + lq;  // 16-byte chunk of the row (0..95)
+        *reinterpret_cast<f32x4*>(mine + lr * BN + ((c ^ lr) << 2)) = acc[r][j];
+      }
+      lds_barrier();
 #pragma unroll 1
-    for (int p = 0; p < 6; ++p) {
-      const int q = p * 256 + tid;
-      const int row = q / 48, ch = q - row * 48;  // row of the round (0..31), 8-column chunk (0..47)
-      const int half = row >> 4, lrow = row & 15;
-      const float* src = reinterpret_cast<const float*>((r & 1) ? (half ? b1 : b0) : (half ? a1 : a0));
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(src + lrow * BN + (((2 * ch) ^ lrow) << 2));
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + lrow * BN + (((2 * ch + 1) ^ lrow) << 2));
-      const int m = m0 + half * (BM / 2) + 16 * r + lrow, n = n0 + 8 * ch;
-      if (m < g.M && n < g.N) store_chunk8<EPI>(g, m, n, lo, hi);
+      for (int p = 0; p < 6; ++p) {
+        const int q = p * 256 + tid;
+        const int row = q / 48, ch = q - row * 48;  // row of the round (0..31), 8-column chunk (0..47)
+        const int half = row >> 4, lrow = row & 15;
+        const float* src = reinterpret_cast<const float*>((r & 1) ? (half ? b1 : b0) : (half ? a1 : a0));
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(src + lrow * BN + (((2 * ch) ^ lrow) << 2));
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + lrow * BN + (((2 * ch + 1) ^ lrow) << 2));
+        const int m = m0 + half * (BM / 2) + 16 * r + lrow, n = n0 + 8 * ch;
+        if (m < g.M && n < g.N) store_chunk8<EPI>(g, m, n, lo, hi);
+      }
     }
   }
 }

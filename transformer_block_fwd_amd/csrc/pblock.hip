@@ -310,8 +310,34 @@ struct TailPending {
   GemmSched sk;
 };
 
+// Whether a launch takes the GEMM kernels' direct (lane-swap, no LDS) epilogue: the plain
+// forward forms, with no bias, rotary step, saved pre-activation, tanh GeLU or residual.
+template <int EPI>
+bool gemm_epilogue_direct_host(const GemmArgs& g) {
+  if constexpr (EPI == kEpiSplitGelu)
+    return g.bias == nullptr && g.rope_n == 0 && g.pre == nullptr && g.gelu_tanh == 0;
+  else if constexpr (EPI == kEpiResidual)
+    return g.bias == nullptr && g.resid == nullptr;
+  else
+    return false;
+}
+
+// One launch of gemm_bf16_kernel<EPI, BM, false, BN> in its direct-epilogue form when `direct`.
+template <int EPI, int BM, int BN>
+void launch_gemm_form(bool direct, unsigned grid, hipStream_t s, const GemmArgs& g, const GemmSched& sk) {
+  if constexpr (EPI == kEpiSplitGelu || EPI == kEpiResidual) {
+    if (direct) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, false, BN, true>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk,
+                         RowPublish{});
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, false, BN>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk, RowPublish{});
+}
+
 template <int EPI>
 void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s, TailPending* defer = nullptr) {
+  const bool direct = gemm_epilogue_direct_host<EPI>(g);
   GemmSched sk;
   sk.partials = scr.partials;
   sk.wave_units = scr.G;
@@ -329,7 +355,10 @@ void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s, Ta
       sk.dp_units = sk.tiles_m * tiles_nw;
       sk.tail = 0;
       sk.split = 1;
-      hipLaunchKernelGGL((gemm_bf16_wide_kernel<EPI>), dim3(unsigned(sk.dp_units)), dim3(kGemmThreads), 0, s, g, sk);
+      if (direct)
+        hipLaunchKernelGGL((gemm_bf16_wide_kernel<EPI, true>), dim3(unsigned(sk.dp_units)), dim3(kGemmThreads), 0, s, g, sk);
+      else
+        hipLaunchKernelGGL((gemm_bf16_wide_kernel<EPI>), dim3(unsigned(sk.dp_units)), dim3(kGemmThreads), 0, s, g, sk);
       return;
     }
   }
@@ -341,8 +370,7 @@ void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s, Ta
     sk.dp_units = sk.tiles_m * tiles_n192;
     sk.tail = 0;
     sk.split = 1;
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 256, false, 192>), dim3(unsigned(sk.dp_units)), dim3(kGemmThreads), 0, s, g,
-                       sk, RowPublish{});
+    launch_gemm_form<EPI, 256, 192>(direct, unsigned(sk.dp_units), s, g, sk);
     return;
   }
   if (p.tail > 0 && p.split == 2 && p.dp_units > 0) {
@@ -353,19 +381,18 @@ void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s, Ta
     sk.dp_units = p.dp_units;
     sk.tail = 0;
     sk.split = 1;
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(unsigned(p.dp_units)), dim3(kGemmThreads), 0, s, g, sk, RowPublish{});
+    launch_gemm_form<EPI, 256, 256>(direct, unsigned(p.dp_units), s, g, sk);
     GemmSched sh = sk;
     sh.dp_units = 2 * p.tail;
     sh.unit_base = p.dp_units;
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 128>), dim3(unsigned(sh.dp_units)), dim3(kGemmThreads), 0, s, g, sh,
-                       RowPublish{});
+    launch_gemm_form<EPI, 128, 256>(direct, unsigned(sh.dp_units), s, g, sh);
     return;
   }
   sk.dp_units = p.dp_units;
   sk.tail = p.tail;
   sk.split = p.split;
   const unsigned grid = unsigned(p.dp_units + p.tail * p.split);
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk, RowPublish{});
+  launch_gemm_form<EPI, 256, 256>(direct, grid, s, g, sk);
   if (p.tail > 0) {
     if (EPI == kEpiSplitGelu && defer != nullptr) {
       // the reduce writes only FC1 columns when every tail tile starts at or past nsplit
