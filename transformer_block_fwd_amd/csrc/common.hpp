@@ -39,9 +39,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
 }
 
+// Sum over the 64 lanes of a wavefront without LDS: quad butterflies and row rotations by DPP
+// inside each 16-lane row, then the v_permlane16_swap / v_permlane32_swap exchanges across rows.
+// Every lane ends with the total; the order of the additions differs between lanes, so lanes may
+// differ in the last bit (callers read one lane).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  v += dpp_f32<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x124>(v);  // row_ror 4
+  v += dpp_f32<0x128>(v);  // row_ror 8
+  const uint32_t u16 = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u16, u16, false, false);  // rows 0 <-> 1, 2 <-> 3
+  v += __uint_as_float((threadIdx.x & 16) ? r16[0] : r16[1]);
+  const uint32_t u32 = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u32, u32, false, false);  // lanes l <-> l ^ 32
+  v += __uint_as_float((threadIdx.x & 32) ? r32[0] : r32[1]);
   return v;
 }
 
