@@ -353,10 +353,30 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI
   }
 }
 
+// Whether a launch takes a GEMM's direct (lane-swap, no LDS) epilogue form: the plain forms, with
+// no bias, rotary step, saved pre-activation, tanh GeLU or residual, and fp32 output.
+template <int EPI>
+__host__ __device__ inline bool gemm_direct_ok(const GemmArgs& g) {
+  if constexpr (EPI == kEpiSplitGelu)
+    return g.bias == nullptr && g.rope_n == 0 && g.pre == nullptr && g.gelu_tanh == 0;
+  else if constexpr (EPI == kEpiResidual)
+    return g.bias == nullptr && g.resid == nullptr;
+  else if constexpr (EPI == kEpiF32)
+    return g.bias == nullptr;
+  else
+    return false;
+}
+
 // 8 consecutive columns n .. n+7 of row m for the direct epilogue's forms: Q|K|V columns stored
-// as they are, FC1 columns through the exact GeLU, or the output GEMM's plain rounding.
+// as they are, FC1 columns through the exact GeLU, the output GEMM's plain rounding, or fp32.
 template <int EPI>
 __device__ __forceinline__ void store_plain8(const GemmArgs& g, int m, int n, const f32x4& lo, const f32x4& hi) {
+  if constexpr (EPI == kEpiF32) {
+    f32x4* o = reinterpret_cast<f32x4*>(g.out_f32 + int64_t(m) * g.ld0 + n);
+    o[0] = lo;
+    o[1] = hi;
+    return;
+  }
   float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   uint16_t* dst;
   if constexpr (EPI == kEpiSplitGelu) {
@@ -374,9 +394,9 @@ __device__ __forceinline__ void store_plain8(const GemmArgs& g, int m, int n, co
   *reinterpret_cast<u32x4*>(dst) = o;
 }
 
-// Epilogue without LDS staging, for launches with no bias, rotary step, saved pre-activation,
-// tanh GeLU or residual (the host picks the kernel form: with both epilogues in one kernel the
-// register allocator spills accumulators), and their split-K partials.
+// Epilogue without LDS staging, for launches that gemm_direct_ok accepts (the host picks the
+// kernel form: with both epilogues in one kernel the register allocator spills accumulators), and
+// their split-K partials.
 // For every 16-row block i and pair of 16-column blocks (2 jp, 2 jp + 1), one v_permlane16_swap
 // per accumulator register exchanges 16-lane rows between the two blocks' accumulators: lane l
 // of block j holds row l % 16, columns 4 (l / 16) + 0..3; after the swap the first register set
@@ -418,7 +438,8 @@ template <int EPI, int BM = kGemmBM, bool PUB = false, int BN = kGemmBN, bool DI
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs g, GemmSched sk, RowPublish pub) {
   static_assert(BM == 256 || BM == 128, "tile height 256 or 128");
   static_assert(BN == 256 || (BN == 192 && BM == 256 && !PUB), "tile width 256, or 192 for whole waves");
-  static_assert(!DIRECT || ((EPI == kEpiSplitGelu || EPI == kEpiResidual) && !PUB), "direct epilogue forms");
+  static_assert(!DIRECT || ((EPI == kEpiSplitGelu || EPI == kEpiResidual || EPI == kEpiF32) && !PUB),
+                "direct epilogue forms");
   constexpr int BK = kGemmBK, NT = kGemmThreads;
   constexpr int MI = BM / 32, NJ = BN / 32;  // 16x16 MFMA tiles per wavefront (BM/2 x BN/2)
   constexpr int P = MI * NJ / 2;       // MFMAs per phase (half a 32-deep k-step)

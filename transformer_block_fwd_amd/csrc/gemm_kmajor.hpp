@@ -12,7 +12,7 @@
 
 namespace pblk {
 
-template <int EPI, bool AK>
+template <int EPI, bool AK, bool DIRECT = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g, GemmSched sk) {
   constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, NT = kGemmThreads;
   constexpr int MI = 8, NJ = 8;   // 16x16 MFMA tiles per wavefront (128 x 128)
@@ -206,8 +206,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g
 
   // Epilogue: split-K chunks store their fp32 partial tile, every other tile its outputs.
   float* part = tl >= 0 ? sk.partials + int64_t(tl * sk.split + chunk) * (BM * BN) : nullptr;
-  lds_barrier();  // every wave is past its last fragment read
-  gemm_epilogue<EPI, BM>(g, acc, a0, b0, a1, b1, part, m0, n0, wm, wn);
+  if constexpr (DIRECT) {
+    gemm_epilogue_direct<EPI, BM, MI, NJ, BN>(g, acc, part, m0, n0, wm, wn);
+  } else {
+    lds_barrier();  // every wave is past its last fragment read
+    gemm_epilogue<EPI, BM>(g, acc, a0, b0, a1, b1, part, m0, n0, wm, wn);
+  }
 }
 
 template <int EPI, bool AK>
@@ -229,7 +233,14 @@ void launch_gemm_kmajor(const GemmArgs& g, float* partials, int G, hipStream_t s
     sk.tail = 0;
   }
   const unsigned grid = unsigned(sk.dp_units + sk.tail * sk.split);
-  hipLaunchKernelGGL((gemm_kmajor_kernel<EPI, AK>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
+  bool launched = false;
+  if constexpr (EPI == kEpiResidual || EPI == kEpiF32) {
+    if (gemm_direct_ok<EPI>(g)) {  // the lane-swap epilogue (the weight gradients, du)
+      hipLaunchKernelGGL((gemm_kmajor_kernel<EPI, AK, true>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
+      launched = true;
+    }
+  }
+  if (!launched) hipLaunchKernelGGL((gemm_kmajor_kernel<EPI, AK>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
   if (sk.tail > 0)
     hipLaunchKernelGGL((gemm_bf16_tail_reduce_kernel<EPI>), dim3(unsigned(sk.tail * 32)), dim3(256), 0, s, g, sk);
 }

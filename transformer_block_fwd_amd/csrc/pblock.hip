@@ -310,18 +310,6 @@ struct TailPending {
   GemmSched sk;
 };
 
-// Whether a launch takes the GEMM kernels' direct (lane-swap, no LDS) epilogue: the plain
-// forward forms, with no bias, rotary step, saved pre-activation, tanh GeLU or residual.
-template <int EPI>
-bool gemm_epilogue_direct_host(const GemmArgs& g) {
-  if constexpr (EPI == kEpiSplitGelu)
-    return g.bias == nullptr && g.rope_n == 0 && g.pre == nullptr && g.gelu_tanh == 0;
-  else if constexpr (EPI == kEpiResidual)
-    return g.bias == nullptr && g.resid == nullptr;
-  else
-    return false;
-}
-
 // One launch of gemm_bf16_kernel<EPI, BM, false, BN> in its direct-epilogue form when `direct`.
 template <int EPI, int BM, int BN>
 void launch_gemm_form(bool direct, unsigned grid, hipStream_t s, const GemmArgs& g, const GemmSched& sk) {
@@ -337,7 +325,7 @@ void launch_gemm_form(bool direct, unsigned grid, hipStream_t s, const GemmArgs&
 
 template <int EPI>
 void launch_gemm_bf16(const GemmArgs& g, const SkScratch& scr, hipStream_t s, TailPending* defer = nullptr) {
-  const bool direct = gemm_epilogue_direct_host<EPI>(g);
+  const bool direct = gemm_direct_ok<EPI>(g);
   GemmSched sk;
   sk.partials = scr.partials;
   sk.wave_units = scr.G;
