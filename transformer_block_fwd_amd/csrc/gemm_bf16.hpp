@@ -57,10 +57,11 @@
 // that XCD's L2.
 //
 // Epilogue, two forms chosen by the host (template parameter DIRECT):
-//   direct, for launches with no bias, rotary step, saved pre-activation, tanh GeLU or residual
-//     (the plain forward) and their split-K partials: one v_permlane16_swap per accumulator
-//     register pairs up two 16-column MFMA blocks so that every lane holds 8 consecutive
-//     columns of one row, stored with one 16-byte write (no LDS, no barriers);
+//   direct, for launches with no bias, rotary step, tanh GeLU or residual (the plain and the
+//     training forward, the weight-gradient GEMMs, fp32 output) and their split-K partials: one
+//     v_permlane16_swap per accumulator register pairs up two 16-column MFMA blocks so that
+//     every lane holds 8 consecutive columns of one row, stored with one 16-byte write (no LDS,
+//     no barriers);
 //   staged, for the rest: the accumulators go out through LDS in four rounds of 64 rows
 //     (fp32, chunk-permuted), so every global store is a full 16-byte piece of a row and a
 //     wavefront writes whole 512-byte rows.
@@ -354,11 +355,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI
 }
 
 // Whether a launch takes a GEMM's direct (lane-swap, no LDS) epilogue form: the plain forms, with
-// no bias, rotary step, saved pre-activation, tanh GeLU or residual, and fp32 output.
+// no bias, rotary step, tanh GeLU or residual (the saved pre-activation of the training forward is
+// allowed), and fp32 output.
 template <int EPI>
 __host__ __device__ inline bool gemm_direct_ok(const GemmArgs& g) {
   if constexpr (EPI == kEpiSplitGelu)
-    return g.bias == nullptr && g.rope_n == 0 && g.pre == nullptr && g.gelu_tanh == 0;
+    return g.bias == nullptr && g.rope_n == 0 && g.gelu_tanh == 0;
   else if constexpr (EPI == kEpiResidual)
     return g.bias == nullptr && g.resid == nullptr;
   else if constexpr (EPI == kEpiF32)
@@ -368,7 +370,8 @@ __host__ __device__ inline bool gemm_direct_ok(const GemmArgs& g) {
 }
 
 // 8 consecutive columns n .. n+7 of row m for the direct epilogue's forms: Q|K|V columns stored
-// as they are, FC1 columns through the exact GeLU, the output GEMM's plain rounding, or fp32.
+// as they are, FC1 columns through the exact GeLU (their pre-activation stored too when the
+// training forward asks for it), the output GEMM's plain rounding, or fp32.
 template <int EPI>
 __device__ __forceinline__ void store_plain8(const GemmArgs& g, int m, int n, const f32x4& lo, const f32x4& hi) {
   if constexpr (EPI == kEpiF32) {
@@ -383,6 +386,11 @@ __device__ __forceinline__ void store_plain8(const GemmArgs& g, int m, int n, co
     if (n < g.nsplit) {
       dst = g.out0 + int64_t(m) * g.ld0 + n;
     } else {
+      if (g.pre != nullptr) {
+        const u32x4 pw = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7])};
+        *reinterpret_cast<u32x4*>(g.pre + int64_t(m) * g.ld_pre + (n - g.nsplit)) = pw;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = gelu_erf_bf16out(v[e]);
       dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
