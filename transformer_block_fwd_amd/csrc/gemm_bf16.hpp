@@ -58,10 +58,10 @@
 //
 // Epilogue, two forms chosen by the host (template parameter DIRECT):
 //   direct, for launches with no bias, rotary step, tanh GeLU or residual (the plain and the
-//     training forward, the weight-gradient GEMMs, fp32 output) and their split-K partials: one
-//     v_permlane16_swap per accumulator register pairs up two 16-column MFMA blocks so that
-//     every lane holds 8 consecutive columns of one row, stored with one 16-byte write (no LDS,
-//     no barriers);
+//     training forward, every gradient GEMM: weights, fp32 output, GeLU backward) and their
+//     split-K partials: one v_permlane16_swap per accumulator register pairs up two 16-column
+//     MFMA blocks so that every lane holds 8 consecutive columns of one row, stored with one
+//     16-byte write (no LDS, no barriers);
 //   staged, for the rest: the accumulators go out through LDS in four rounds of 64 rows
 //     (fp32, chunk-permuted), so every global store is a full 16-byte piece of a row and a
 //     wavefront writes whole 512-byte rows.
@@ -356,14 +356,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[MI
 
 // Whether a launch takes a GEMM's direct (lane-swap, no LDS) epilogue form: the plain forms, with
 // no bias, rotary step, tanh GeLU or residual (the saved pre-activation of the training forward is
-// allowed), and fp32 output.
+// allowed), fp32 output, and the GeLU-backward form.
 template <int EPI>
 __host__ __device__ inline bool gemm_direct_ok(const GemmArgs& g) {
   if constexpr (EPI == kEpiSplitGelu)
     return g.bias == nullptr && g.rope_n == 0 && g.gelu_tanh == 0;
   else if constexpr (EPI == kEpiResidual)
     return g.bias == nullptr && g.resid == nullptr;
-  else if constexpr (EPI == kEpiF32)
+  else if constexpr (EPI == kEpiF32 || EPI == kEpiGeluBwd)
     return g.bias == nullptr;
   else
     return false;
@@ -371,7 +371,8 @@ __host__ __device__ inline bool gemm_direct_ok(const GemmArgs& g) {
 
 // 8 consecutive columns n .. n+7 of row m for the direct epilogue's forms: Q|K|V columns stored
 // as they are, FC1 columns through the exact GeLU (their pre-activation stored too when the
-// training forward asks for it), the output GEMM's plain rounding, or fp32.
+// training forward asks for it), the output GEMM's plain rounding, fp32, or the GeLU-backward
+// form (FC1 columns scaled by GeLU' of the saved pre-activation).
 template <int EPI>
 __device__ __forceinline__ void store_plain8(const GemmArgs& g, int m, int n, const f32x4& lo, const f32x4& hi) {
   if constexpr (EPI == kEpiF32) {
@@ -393,6 +394,18 @@ __device__ __forceinline__ void store_plain8(const GemmArgs& g, int m, int n, co
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = gelu_erf_bf16out(v[e]);
+      dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
+    }
+  } else if constexpr (EPI == kEpiGeluBwd) {
+    if (n < g.nsplit) {
+      dst = g.out0 + int64_t(m) * g.ld0 + n;
+    } else {
+      const u32x4 fr = *reinterpret_cast<const u32x4*>(g.pre + int64_t(m) * g.ld_pre + (n - g.nsplit));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] *= gelu_erf_grad(__uint_as_float(fr[e] << 16));
+        v[2 * e + 1] *= gelu_erf_grad(__uint_as_float(fr[e] & 0xFFFF0000u));
+      }
       dst = g.out1 + int64_t(m) * g.ld1 + g.off1 + (n - g.nsplit);
     }
   } else {

@@ -234,8 +234,8 @@ void launch_gemm_kmajor(const GemmArgs& g, float* partials, int G, hipStream_t s
   }
   const unsigned grid = unsigned(sk.dp_units + sk.tail * sk.split);
   bool launched = false;
-  if constexpr (EPI == kEpiResidual || EPI == kEpiF32) {
-    if (gemm_direct_ok<EPI>(g)) {  // the lane-swap epilogue (the weight gradients, du)
+  if constexpr (EPI == kEpiResidual || EPI == kEpiF32 || EPI == kEpiGeluBwd) {
+    if (gemm_direct_ok<EPI>(g)) {  // the lane-swap epilogue (every gradient GEMM without a bias)
       hipLaunchKernelGGL((gemm_kmajor_kernel<EPI, AK, true>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
       launched = true;
     }
