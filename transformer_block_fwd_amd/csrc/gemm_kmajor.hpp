@@ -12,8 +12,9 @@
 
 namespace pblk {
 
-template <int EPI, bool AK, bool DIRECT = false>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g, GemmSched sk) {
+// One workgroup's tile (or split-K chunk) bid of the schedule sk.
+template <int EPI, bool AK, bool DIRECT>
+__device__ __forceinline__ void gemm_kmajor_tile(const GemmArgs& g, const GemmSched& sk, const int bid) {
   constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, NT = kGemmThreads;
   constexpr int MI = 8, NJ = 8;   // 16x16 MFMA tiles per wavefront (128 x 128)
   constexpr int P = MI * NJ / 2;  // MFMAs per phase (half a 32-deep k-step)
@@ -31,13 +32,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g
   const int wm = wave >> 1, wn = wave & 1;
 
   int L, kb, ke, tl = -1, chunk = 0;
-  if (int(blockIdx.x) < sk.dp_units) {
-    L = xcd_remap(blockIdx.x, sk.dp_units);
+  if (bid < sk.dp_units) {
+    L = xcd_remap(bid, sk.dp_units);
     kb = 0;
     ke = sk.KT;
   } else {
     const int nu = sk.tail * sk.split;
-    const int u = xcd_remap(blockIdx.x - sk.dp_units, nu);
+    const int u = xcd_remap(bid - sk.dp_units, nu);
     chunk = u / sk.tail;
     tl = u % sk.tail;
     L = sk.dp_units + tl;
@@ -214,8 +215,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g
   }
 }
 
-template <int EPI, bool AK>
-void launch_gemm_kmajor(const GemmArgs& g, float* partials, int G, hipStream_t s) {
+template <int EPI, bool AK, bool DIRECT = false>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_kernel(GemmArgs g, GemmSched sk) {
+  gemm_kmajor_tile<EPI, AK, DIRECT>(g, sk, int(blockIdx.x));
+}
+
+// Two independent K-major GEMMs in one launch (the two weight gradients): workgroups
+// 0 .. s0.dp_units-1 compute the first, the rest the second, so that the second's tiles fill the
+// compute units the first's last partial wave leaves idle.  Both schedules hold whole tiles only.
+template <int EPI, bool AK, bool DIRECT>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kmajor_pair_kernel(GemmArgs g0, GemmSched s0, GemmArgs g1,
+                                                                            GemmSched s1) {
+  const int bid = int(blockIdx.x);
+  if (bid < s0.dp_units)
+    gemm_kmajor_tile<EPI, AK, DIRECT>(g0, s0, bid);
+  else
+    gemm_kmajor_tile<EPI, AK, DIRECT>(g1, s1, bid - s0.dp_units);
+}
+
+// Work decomposition of one K-major GEMM on G resident workgroups: whole waves of tiles, then the
+// remaining tiles in k-chunks when they fill at most half a wave.
+inline GemmSched gemm_kmajor_sched(const GemmArgs& g, float* partials, int G) {
   GemmSched sk;
   sk.partials = partials;
   sk.unit_base = 0;
@@ -232,6 +252,12 @@ void launch_gemm_kmajor(const GemmArgs& g, float* partials, int G, hipStream_t s
     sk.dp_units = int(T);
     sk.tail = 0;
   }
+  return sk;
+}
+
+template <int EPI, bool AK>
+void launch_gemm_kmajor(const GemmArgs& g, float* partials, int G, hipStream_t s) {
+  const GemmSched sk = gemm_kmajor_sched(g, partials, G);
   const unsigned grid = unsigned(sk.dp_units + sk.tail * sk.split);
   bool launched = false;
   if constexpr (EPI == kEpiResidual || EPI == kEpiF32 || EPI == kEpiGeluBwd) {
@@ -243,6 +269,23 @@ void launch_gemm_kmajor(const GemmArgs& g, float* partials, int G, hipStream_t s
   if (!launched) hipLaunchKernelGGL((gemm_kmajor_kernel<EPI, AK>), dim3(grid), dim3(kGemmThreads), 0, s, g, sk);
   if (sk.tail > 0)
     hipLaunchKernelGGL((gemm_bf16_tail_reduce_kernel<EPI>), dim3(unsigned(sk.tail * 32)), dim3(256), 0, s, g, sk);
+}
+
+// Two independent K-major GEMMs: one launch when neither leaves tiles to split along k, both take
+// the direct epilogue and a partial wave is left over; otherwise one launch after the other.
+template <int EPI, bool AK>
+void launch_gemm_kmajor_pair(const GemmArgs& g0, const GemmArgs& g1, float* partials, int G, hipStream_t s) {
+  if constexpr (EPI == kEpiResidual || EPI == kEpiF32 || EPI == kEpiGeluBwd) {
+    const GemmSched s0 = gemm_kmajor_sched(g0, partials, G), s1 = gemm_kmajor_sched(g1, partials, G);
+    if (s0.tail == 0 && s1.tail == 0 && gemm_direct_ok<EPI>(g0) && gemm_direct_ok<EPI>(g1) &&
+        (s0.dp_units % G != 0 || s1.dp_units % G != 0)) {
+      hipLaunchKernelGGL((gemm_kmajor_pair_kernel<EPI, AK, true>), dim3(unsigned(s0.dp_units + s1.dp_units)),
+                         dim3(kGemmThreads), 0, s, g0, s0, g1, s1);
+      return;
+    }
+  }
+  launch_gemm_kmajor<EPI, AK>(g0, partials, G, s);
+  launch_gemm_kmajor<EPI, AK>(g1, partials, G, s);
 }
 
 }  // namespace pblk

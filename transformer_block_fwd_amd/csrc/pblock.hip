@@ -1503,20 +1503,16 @@ int pblock_backward(pblock_t h, const void* x, const pblock_weights* w, const pb
     // dW_out = dy^T [A | G], dW_in = dz^T u: contractions over the Mp tokens, both operands read
     // K-major in place (token rows M .. Mp-1 zeroed above)
     {
-      GemmArgs g{};
-      g.a = static_cast<const uint16_t*>(dy_rows); g.lda = d;
-      g.b = reinterpret_cast<const uint16_t*>(base + T.ag); g.ldb = dm.k_out;
-      g.M = int(d); g.N = int(dm.k_out); g.K = int(T.Mp);
-      g.out0 = static_cast<uint16_t*>(grads->dw_out); g.ld0 = dm.k_out;
-      launch_gemm_kmajor<kEpiResidual, true>(g, hw.scr.partials, hw.scr.G, s);
-    }
-    {
-      GemmArgs g{};
-      g.a = reinterpret_cast<const uint16_t*>(base + T.dz); g.lda = dm.n_in;
-      g.b = reinterpret_cast<const uint16_t*>(base + T.u); g.ldb = d;
-      g.M = int(dm.n_in); g.N = int(d); g.K = int(T.Mp);
-      g.out0 = static_cast<uint16_t*>(grads->dw_in); g.ld0 = d;
-      launch_gemm_kmajor<kEpiResidual, true>(g, hw.scr.partials, hw.scr.G, s);
+      GemmArgs go{}, gi{};
+      go.a = static_cast<const uint16_t*>(dy_rows); go.lda = d;
+      go.b = reinterpret_cast<const uint16_t*>(base + T.ag); go.ldb = dm.k_out;
+      go.M = int(d); go.N = int(dm.k_out); go.K = int(T.Mp);
+      go.out0 = static_cast<uint16_t*>(grads->dw_out); go.ld0 = dm.k_out;
+      gi.a = reinterpret_cast<const uint16_t*>(base + T.dz); gi.lda = dm.n_in;
+      gi.b = reinterpret_cast<const uint16_t*>(base + T.u); gi.ldb = d;
+      gi.M = int(dm.n_in); gi.N = int(d); gi.K = int(T.Mp);
+      gi.out0 = static_cast<uint16_t*>(grads->dw_in); gi.ld0 = d;
+      launch_gemm_kmajor_pair<kEpiResidual, true>(go, gi, hw.scr.partials, hw.scr.G, s);
     }
     tm.mark(7);
     return launch_status("pblock_backward launch");
