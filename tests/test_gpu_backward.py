@@ -28,6 +28,9 @@ SHAPES = [
     # d = 192 also has the K-major dy reads clamp at the last 8 columns
     ("bwd_whole_tiles", 2, 256, 256, 2, 128, 320, 64, 1),
     ("bwd_whole_tiles_d192", 1, 768, 192, 3, 64, 128, 100, 0),
+    # the two weight-gradient GEMMs in one launch: dW_out 11 x 13 = 143 tiles (an odd count, so
+    # the second GEMM's workgroups start mid-XCD) and dW_in 15 x 11 = 165, each a partial wave
+    ("bwd_paired_wgrad", 1, 2048, 2816, 2, 128, 3072, 256, 0),
     # d = 16384, the largest the backward accepts (Q rows of W_in scaled by 2^-3, see below)
     ("bwd_max_d", 1, 130, 16384, 2, 64, 128, 40, 1),
 ]
