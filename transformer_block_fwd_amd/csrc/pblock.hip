@@ -1362,11 +1362,14 @@ int pblock_forward_train(pblock_t h, const void* x, const pblock_weights* w, con
     InEpi ep;
     ep.pre = base + T.f;
     ep.ld_pre = c.ffn;
+    // as in the plain forward, a split-K reduce of FC1-only tail tiles (which also stores their
+    // pre-activation) runs inside the attention launch
+    TailPending tail;
     run_gemm_in(base + T.u, c.d, w->w_in, c.d, dm.M, dm.n_in, c.d, base + T.qkv, 3 * A, base + T.ag, dm.k_out, A, 3 * A,
-                c.dtype, hw.scr, s, ep);
+                c.dtype, hw.scr, s, ep, &tail);
     tm.mark(1);
     launch_attention(base + T.qkv, 3 * A, base + T.ag, dm.k_out, c.B, c.S, c.H, c.hd, c.W, c.dtype, s, 0, -1,
-                     reinterpret_cast<float*>(base + T.lse));
+                     reinterpret_cast<float*>(base + T.lse), &tail);
     tm.mark(2);
     run_gemm_out(base + T.ag, dm.k_out, w->w_out, dm.k_out, dm.M, c.d, dm.k_out, out, c.add_residual ? x : nullptr,
                  c.dtype, hw.scr, s);
